@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for the three block formats.
+
+This module only draws random numbers and packs them into the byte layouts;
+it holds no dequantisation or dot-product arithmetic.  It is the one module
+that both the HIP path's tests/bench and the CPU checker read their inputs
+from.
+
+Distributions follow the Llama-8B-shaped decode workloads the pages measure:
+
+* Q4_K ("Writing a high performant GEMV + dequant for Metal", section "What is
+  a weight block?"): 144-byte super-blocks of 256 weights.  fp16 ``d`` and
+  ``dmin`` ~ U(1e-3, 1e-2) rounded to nearest-even, the 12 packed scale/min
+  bytes uniform (every 6-bit scale and min then uniform on 0..63), the 128
+  nibble bytes uniform.
+* NVFP4 W4A16 (Mojo ``fp4_gemv`` module page): nibble bytes uniform (all 16
+  E2M1 codes), one E4M3 scale per 16 weights drawn as |N(0, 0.05)| and
+  rounded to the nearest E4M3 value by torch's ``float8_e4m3fn`` cast.
+* TQ1_0 ("metal: TQ1_0 kernel performance", section 1): 54-byte blocks of
+  ``qs[48] | qh[4] | d``.  Trits iid uniform over {-1, 0, +1}, which is the
+  same as drawing each qs byte uniformly from the 243 five-trit codes and
+  each qh byte uniformly from the 81 four-trit codes (fifth trit zero).
+  ``d`` ~ U(1e-2, 5e-2) in fp16.
+
+Activations are fp16 (Q4_K, TQ1_0) or bf16 (NVFP4) draws of N(0, 1).
+
+All draws use numpy's PCG64 so a seed names one input exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q4K_BLOCK_BYTES = 144
+TQ1_BLOCK_BYTES = 54
+QK = 256  # weights per Q4_K / TQ1_0 block
+NVFP4_SF = 16  # weights per E4M3 scale
+
+# Seeds used by the tests and the bench: weight seed = 1000 + case,
+# activation seed = 2000 + case.
+W_SEED = 1000
+X_SEED = 2000
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def tq1_codes(ntrits: int) -> np.ndarray:
+    """Byte codes of all base-3 tuples of ``ntrits`` trits (most significant
+    first), padded with zero trits to five.  Code of value v = ceil(256 v / 243),
+    the smallest byte whose digits read back as v (an encoder, not a decoder)."""
+    vals = np.arange(3 ** ntrits, dtype=np.int64) * 3 ** (5 - ntrits)
+    return ((256 * vals + 242) // 243).astype(np.uint8)
+
+
+def x_f16(k: int, seed: int) -> np.ndarray:
+    """fp16 activations ~N(0,1) (round to nearest even), as uint16 bits."""
+    return _rng(seed).standard_normal(k).astype(np.float16).view(np.uint16)
+
+
+def x_bf16(k: int, seed: int) -> np.ndarray:
+    """bf16 activations ~N(0,1) (round to nearest even), as uint16 bits."""
+    import torch
+
+    v = torch.from_numpy(_rng(seed).standard_normal(k).astype(np.float32))
+    return v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def q4k_weights(n: int, k: int, seed: int) -> np.ndarray:
+    """Q4_K matrix [n, k/256 * 144] uint8, row-major, K contiguous."""
+    assert k % QK == 0
+    nb = k // QK
+    rng = _rng(seed)
+    blk = rng.integers(0, 256, size=(n, nb, Q4K_BLOCK_BYTES), dtype=np.uint8)
+    d = rng.uniform(1e-3, 1e-2, size=(n, nb)).astype(np.float16)
+    dmin = rng.uniform(1e-3, 1e-2, size=(n, nb)).astype(np.float16)
+    blk[:, :, 0:2] = d.view(np.uint8).reshape(n, nb, 2)
+    blk[:, :, 2:4] = dmin.view(np.uint8).reshape(n, nb, 2)
+    return blk.reshape(n, nb * Q4K_BLOCK_BYTES)
+
+
+def nvfp4_weights(n: int, k: int, seed: int, sigma: float = 0.05) -> np.ndarray:
+    """NVFP4 matrix as ONE buffer: n*k/2 nibble bytes ([n][k/2], even element
+    in the low nibble) followed by n*k/16 E4M3 scale bytes ([n][k/16])."""
+    import torch
+
+    assert k % 32 == 0
+    rng = _rng(seed)
+    nib = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    s = np.abs(rng.standard_normal((n, k // NVFP4_SF)) * sigma).astype(np.float32)
+    sc = torch.from_numpy(s).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.concatenate([nib.reshape(-1), sc.reshape(-1)])
+
+
+def tq1_weights(n: int, k: int, seed: int) -> np.ndarray:
+    """TQ1_0 matrix [n, k/256 * 54] uint8: per block qs[48] | qh[4] | fp16 d."""
+    assert k % QK == 0
+    nb = k // QK
+    rng = _rng(seed)
+    c5 = tq1_codes(5)
+    c4 = tq1_codes(4)
+    blk = np.empty((n, nb, TQ1_BLOCK_BYTES), dtype=np.uint8)
+    blk[:, :, 0:48] = c5[rng.integers(0, c5.size, size=(n, nb, 48))]
+    blk[:, :, 48:52] = c4[rng.integers(0, c4.size, size=(n, nb, 4))]
+    d = rng.uniform(1e-2, 5e-2, size=(n, nb)).astype(np.float16)
+    blk[:, :, 52:54] = d.view(np.uint8).reshape(n, nb, 2)
+    return blk.reshape(n, nb * TQ1_BLOCK_BYTES)
+
+
+def weights(fmt: str, n: int, k: int, seed: int) -> np.ndarray:
+    return {"q4k": q4k_weights, "nvfp4": nvfp4_weights, "tq1": tq1_weights}[fmt](n, k, seed)
+
+
+def activations(fmt: str, k: int, seed: int) -> np.ndarray:
+    return x_bf16(k, seed) if fmt == "nvfp4" else x_f16(k, seed)
+
+
+def weight_bytes(fmt: str, n: int, k: int) -> int:
+    """Bytes of the packed weight buffer."""
+    if fmt == "q4k":
+        return n * (k // QK) * Q4K_BLOCK_BYTES
+    if fmt == "tq1":
+        return n * (k // QK) * TQ1_BLOCK_BYTES
+    if fmt == "nvfp4":
+        return n * k // 2 + n * k // NVFP4_SF
+    raise ValueError(fmt)

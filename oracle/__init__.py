@@ -1,0 +1,117 @@
+"""ctypes front end of the fp64 CPU oracle (``oracle.c``).
+
+Test infrastructure only: the test suite, ``__graft_entry__.smoke()`` and the
+bench's CPU-baseline leg are its only users; the HIP library never imports it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FMT = {"q4k": 0, "nvfp4": 1, "tq1": 2}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile oracle.c with gcc: -O2, no fast-math, no FMA contraction, OpenMP."""
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-fPIC", "-shared", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_f16.restype = ctypes.c_double
+    lib.oracle_f16.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16.restype = ctypes.c_double
+    lib.oracle_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3.restype = ctypes.c_double
+    lib.oracle_e4m3.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1.restype = ctypes.c_double
+    lib.oracle_e2m1.argtypes = [ctypes.c_uint8]
+    lib.oracle_tq1_digit.restype = ctypes.c_int
+    lib.oracle_tq1_digit.argtypes = [ctypes.c_uint8, ctypes.c_int]
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_dequant.argtypes = [ctypes.c_int, P, I64, I64, P]
+    lib.oracle_gemv.argtypes = [ctypes.c_int, P, P, I64, I64, P, I64, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def f16(h: int) -> float:
+    return _load().oracle_f16(h)
+
+
+def bf16(h: int) -> float:
+    return _load().oracle_bf16(h)
+
+
+def e4m3(c: int) -> float:
+    return _load().oracle_e4m3(c)
+
+
+def e2m1(n: int) -> float:
+    return _load().oracle_e2m1(n)
+
+
+def tq1_digit(b: int, k: int) -> int:
+    return _load().oracle_tq1_digit(b, k)
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def set_threads(t: int) -> None:
+    _load().oracle_set_threads(t)
+
+
+def dequant(fmt: str, w: np.ndarray, n: int, k: int) -> np.ndarray:
+    """fp64 weights [n, k] of the packed matrix ``w``."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    out = np.empty((n, k), dtype=np.float64)
+    _load().oracle_dequant(FMT[fmt], _ptr(w), n, k, _ptr(out))
+    return out
+
+
+def gemv(fmt: str, w: np.ndarray, x: np.ndarray, n: int, k: int, rows=None):
+    """(y, a): fp64 y[r] = sum_i x_i w_ri and a[r] = sum_i |x_i w_ri| for the
+    listed rows (all rows when ``rows`` is None).  ``x`` holds uint16 bits."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    assert x.size == k
+    if rows is None:
+        cnt = n
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < n)
+        cnt = rows.size
+        rp = _ptr(rows)
+    y = np.empty(cnt, dtype=np.float64)
+    a = np.empty(cnt, dtype=np.float64)
+    if cnt:
+        _load().oracle_gemv(FMT[fmt], _ptr(w), _ptr(x), n, k, rp, cnt, _ptr(y), _ptr(a))
+    return y, a
