@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Throughput of the batch-1 fused dequantise + GEMV on one MI355X.
+
+One step = one Q4_K GEMV y = x . dequant(W)^T at N = 4096 rows, K = 14336 (the
+Llama-8B down-projection shape) on synthetic seeded weights, i.e. every row of
+the hot path: weight stream, activation staging, block decode, factored dot,
+reductions, store.  Inputs are resident in HBM before the timed region.  Each
+step reads a different one of R copies of the weights (R * 33 MB well above
+the 256 MB Infinity Cache), so every launch streams its weights from HBM.
+
+Printed: ONE JSON line with the metric (achieved HBM GB/s of the kernel over
+the algorithmic bytes weights + x + y), the roofline object of the dominant
+kernel, the CPU baseline (the fp64 oracle on the host cores) and extra context
+(pure-read ceiling over the same bytes, the other formats' shapes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+METRIC = "achieved HBM GB/s (% of ~8 TB/s peak), M=1 Q4_K GEMV N=4096 K=14336"
+HBM_PEAK_GBPS = 8000.0
+
+# (format, rows, K, description) of the measured shapes
+MAIN = ("q4k", 4096, 14336, "Q4_K GEMV M=1, N=4096 x K=14336 (Llama-8B MLP down projection)")
+EXTRA = [
+    ("q4k", 14336, 4096, "Q4_K GEMV M=1, N=14336 x K=4096 (gate/up)"),
+    ("q4k", 4096, 4096, "Q4_K GEMV M=1, N=4096 x K=4096"),
+    ("nvfp4", 4096, 14336, "NVFP4 W4A16 GEMV M=1, N=4096 x K=14336"),
+    ("tq1", 14336, 4096, "TQ1_0 GEMV M=1, N=14336 x K=4096"),
+]
+CASE_SEED = {("q4k", 4096, 4096): 0, ("q4k", 14336, 4096): 1, ("q4k", 4096, 14336): 1,
+             ("nvfp4", 4096, 14336): 2, ("tq1", 14336, 4096): 3}
+
+
+def algorithmic_bytes(fmt: str, n: int, k: int) -> int:
+    """Bytes the method must move once: packed weights + x (2 B/elem) + y (fp32)."""
+    from dequant_gemv_amd import synth
+
+    return synth.weight_bytes(fmt, n, k) + 2 * k + 4 * n
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
+    import numpy as np
+    import torch
+
+    from dequant_gemv_amd import qgemv, synth
+
+    dev = torch.device("cuda:0")
+    seed = CASE_SEED.get((fmt, n, k), 9)
+    w_host = synth.weights(fmt, n, k, synth.W_SEED + seed)
+    x_host = synth.activations(fmt, k, synth.X_SEED + seed)
+    w0 = torch.from_numpy(w_host).to(dev)
+    ws = [w0] + [w0.clone() for _ in range(rotate - 1)]
+    x = torch.from_numpy(x_host.view(np.int16).copy()).to(dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    fn = qgemv.GEMV[fmt]
+    stream = torch.cuda.Stream()
+    s_handle = stream.cuda_stream
+    nbytes = algorithmic_bytes(fmt, n, k)
+
+    def one(i):
+        fn(ws[i % rotate], x, y, n, k, s_handle)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            one(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if launch == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(rotate):
+                one(i)
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        if graph is not None:
+            for _ in range(steps // rotate):
+                graph.replay()
+            for i in range(steps % rotate):
+                one(i)
+        else:
+            for i in range(steps):
+                one(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    res = {
+        "wall_s": wall,
+        "event_ms": ev_ms,
+        "us_per_launch_event": 1e3 * ev_ms / steps,
+        "us_per_step_wall": 1e6 * wall / steps,
+        "bytes": nbytes,
+    }
+    res["gbps_event"] = nbytes / (res["us_per_launch_event"] * 1e-6) / 1e9
+    res["gbps_wall"] = nbytes / (res["us_per_step_wall"] * 1e-6) / 1e9
+
+    if with_ceiling:
+        wb = synth.weight_bytes(fmt, n, k)
+        sink = torch.empty(qgemv.qgemv_read_sink_len(wb), dtype=torch.float32, device=dev)
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                qgemv.qgemv_read_ceiling(ws[i % rotate], wb, sink, s_handle)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(cg, stream=stream):
+            for i in range(rotate):
+                qgemv.qgemv_read_ceiling(ws[i], wb, sink, s_handle)
+        reps = max(1, steps // rotate)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                cg.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * ev0.elapsed_time(ev1) / (reps * rotate)
+        res["ceiling_us"] = us
+        res["ceiling_gbps"] = wb / (us * 1e-6) / 1e9
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(fmt, n, k, budget_s=10.0):
+    """The fp64 oracle as it stands, all host cores, on the same workload."""
+    import numpy as np
+
+    import oracle
+    from dequant_gemv_amd import synth
+
+    seed = CASE_SEED.get((fmt, n, k), 9)
+    w = synth.weights(fmt, n, k, synth.W_SEED + seed)
+    x = synth.activations(fmt, k, synth.X_SEED + seed)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    oracle.set_threads(cores)
+    oracle.gemv(fmt, w, x, n, k)  # warm-up
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start) * cores < budget_s and len(times) < 50:
+        t0 = time.perf_counter()
+        oracle.gemv(fmt, w, x, n, k)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {
+        "value": algorithmic_bytes(fmt, n, k) / t / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"full {n}x{k} {fmt} matrix, median of {len(times)} runs "
+                  f"({t * 1e3:.1f} ms each, fp64 scalar dequantise-then-dot, OpenMP over rows)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3200)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--rotate", type=int, default=32, help="distinct weight copies cycled through")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other formats' shapes")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--fmt", default=None, help="measure only this format (q4k, nvfp4, tq1) at N,K")
+    ap.add_argument("--n", type=int, default=None)
+    ap.add_argument("--k", type=int, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dequant_gemv_amd import build, qgemv
+
+    # Provenance: the library must be built from the sources in this tree.
+    want, have = build.build_id(), qgemv.qgemv_build_id()
+    if want != have:
+        print(f"libqgemv.so build id {have} does not match the sources ({want}); rebuild", file=sys.stderr)
+        sys.exit(3)
+
+    fmt, n, k, desc = MAIN
+    if args.fmt:
+        fmt, n, k, desc = args.fmt, args.n or n, args.k or k, f"{args.fmt} GEMV M=1, N={args.n or n} x K={args.k or k}"
+    log(f"[bench] build {have} on {torch.cuda.get_device_name(0)}; main {fmt} {n}x{k}")
+    main_res = measure_gpu(fmt, n, k, args.steps, args.warmup, args.rotate, args.launch)
+    log(f"[bench] main: {main_res['us_per_launch_event']:.3f} us/launch, {main_res['gbps_event']:.1f} GB/s "
+        f"(ceiling {main_res['ceiling_gbps']:.1f} GB/s)")
+
+    extra = {}
+    if not args.no_extra and not args.fmt:
+        for efmt, en, ek, edesc in EXTRA:
+            r = measure_gpu(efmt, en, ek, max(args.rotate, args.steps // 4), args.warmup, args.rotate, args.launch)
+            extra[f"{efmt}_{en}x{ek}"] = {
+                "workload": edesc,
+                "us_per_gemv": round(r["us_per_launch_event"], 3),
+                "gbps": round(r["gbps_event"], 1),
+                "pct_of_hbm_peak": round(100 * r["gbps_event"] / HBM_PEAK_GBPS, 1),
+                "read_ceiling_gbps": round(r["ceiling_gbps"], 1),
+            }
+            log(f"[bench] {efmt} {en}x{ek}: {r['us_per_launch_event']:.3f} us, {r['gbps_event']:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(fmt, n, k)
+        log(f"[bench] cpu oracle: {cpu['value']:.2f} GB/s on {cpu['cores']} threads")
+
+    value = main_res["gbps_wall"]
+    achieved = main_res["gbps_event"]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["us_per_step_wall"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": desc,
+            "format": fmt, "n": n, "k": k,
+            "algorithmic_bytes_per_gemv": main_res["bytes"],
+            "rotated_weight_copies": args.rotate,
+            "launch": "hipGraph of %d launches" % args.rotate if args.launch == "graph" else "eager",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "us_per_gemv": round(main_res["us_per_launch_event"], 3),
+        "read_ceiling": {"gbps": round(main_res["ceiling_gbps"], 1), "us": round(main_res["ceiling_us"], 3),
+                         "note": "pure dwordx4 read of the same weight bytes, same rotation"},
+        "cpu_baseline": cpu,
+        "other_shapes": extra,
+        "build_id": have,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,54 @@
+"""Build libqgemv.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
+
+The library embeds a build id: the SHA-256 of its sources and header, so a
+measurement can check which code it ran (see ``qgemv_build_id``).
+"""
+from __future__ import annotations
+
+import glob
+import hashlib
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libqgemv.so")
+ARCH = "gfx950"
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build_id() -> str:
+    h = hashlib.sha256()
+    files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [os.path.join(INCLUDE, "qgemv.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    out = LIB + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           # no packed-fp32 VALU forms anywhere in the device code
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-result",
+           f"-DQGEMV_BUILD_ID=\"{build_id()}\"",
+           "-I", INCLUDE, "-I", CSRC, *sources(), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stderr)
+    if verbose:
+        print(r.stderr)
+    os.replace(out, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

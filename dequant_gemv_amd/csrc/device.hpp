@@ -1,0 +1,105 @@
+// Device helpers shared by the gfx950 kernels: range-checked buffer loads,
+// packed-type aliases and wave64 reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qgemv {
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr int kWave = 64;
+
+// Raw buffer descriptor over [base, base + bytes).  Loads whose byte range
+// falls outside it return zero instead of touching memory, so ragged tails
+// (last rows, last K-chunk) need no address clamping.  Offsets are 32-bit, so
+// callers rebase `base` per workgroup and keep `bytes` below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ unsigned ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ unsigned short ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ f16x2 as_h2(unsigned v) { return __builtin_bit_cast(f16x2, v); }
+
+// v_dot2_f32_f16: a.x*b.x + a.y*b.y + c with fp32 accumulation.
+__device__ __forceinline__ float dot2h(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
+// v_dot2_f32_bf16
+__device__ __forceinline__ float dot2bf(bf16x2 a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Two E2M1 codes (byte `sel` of v, low nibble first) -> exact bf16 / fp32 pair.
+// The selector must be an immediate; the switch folds once `sel` is a constant.
+__device__ __forceinline__ bf16x2 fp4x2_bf16(unsigned v, int sel) {
+  switch (sel & 3) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
+  }
+}
+__device__ __forceinline__ f32x2 fp4x2_f32(unsigned v, int sel) {
+  switch (sel & 3) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+  }
+}
+
+__device__ __forceinline__ float f16lo(unsigned v) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(unsigned v) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) {
+  int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, v)));
+}
+
+// Reduce R (a power of two <= 64) per-lane partials across the 64 lanes of a
+// wave.  Each halving step exchanges half of the values with the partner lane,
+// so the whole reduction costs about R + log2(64/R) exchanges instead of
+// 6 R.  On return v[0] of lane l holds the total of row l >> (6 - log2 R).
+template <int R, int CNT = R, int S = 32>
+__device__ __forceinline__ void wave_reduce_rows(float (&v)[R]) {
+  static_assert(R >= 1 && R <= 64 && (R & (R - 1)) == 0, "R must be a power of two <= 64");
+  if constexpr (CNT > 1) {
+    constexpr int H = CNT / 2;
+    const bool up = (__lane_id() & S) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      float send = up ? v[i] : v[i + H];
+      float keep = up ? v[i + H] : v[i];
+      v[i] = keep + shfl_xor(send, S);
+    }
+    wave_reduce_rows<R, H, S / 2>(v);
+  } else if constexpr (S >= 1) {
+    v[0] += shfl_xor(v[0], S);
+    wave_reduce_rows<R, 1, S / 2>(v);
+  }
+}
+
+template <int R>
+__device__ __forceinline__ constexpr int log2i() {
+  return R <= 1 ? 0 : 1 + log2i<R / 2>();
+}
+
+}  // namespace qgemv

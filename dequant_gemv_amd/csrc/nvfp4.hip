@@ -1,0 +1,147 @@
+// NVFP4 W4A16 fused dequantise + GEMV and fp32 dequantise for gfx950.
+//
+// Format (Mojo module "fp4_gemv"): E2M1 nibbles with one FP8 E4M3 scale per 16
+// consecutive weights; weight = e2m1 * |scale|; bf16 activations, fp32
+// accumulation.  Buffer: [M][K/2] nibble bytes (even element in the low
+// nibble), then [M][K/16] scale bytes.
+//
+// GEMV work split.  As on that page each lane owns whole 16-weight scale
+// blocks, but on a wave64 the lanes take contiguous 16-byte slices: a wave
+// owns one K-chunk of 2048 weights (1 KiB of nibbles, fully coalesced) for R
+// rows, lane l the 32 weights 32l..32l+31 of the chunk (two scale blocks).
+// gfx950 converts two E2M1 codes to a bf16 pair in one instruction
+// (v_cvt_scalef32_pk_bf16_fp4, scale 1.0: exact) and v_dot2_f32_bf16 multiplies
+// them with the matching bf16 activation pair into an fp32 accumulator, so a
+// weight costs one VALU slot.  |scale| is applied once per 16-weight block
+// (algebraically equal to scaling each weight; only the rounding order moves).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qgemv {
+
+template <int R>
+__global__ __launch_bounds__(512) void nvfp4_gemv_kernel(const uint8_t* __restrict__ w,
+                                                         const uint16_t* __restrict__ x,
+                                                         float* __restrict__ y, int n, int k,
+                                                         int kc, int kw, int rg) {
+  __shared__ float red[16 * 16];
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int kwi = wave % kw;
+  const int rgi = wave / kw;
+  const int64_t nib_row = k / 2, sc_row = k / 16;
+  const int row0 = blockIdx.x * rg * R + rgi * R;
+  const int nrows = max(0, min(R, n - row0));
+  const auto nr = make_rsrc(w + (int64_t)row0 * nib_row, (uint32_t)(nrows * nib_row));
+  const auto sr = make_rsrc(w + (int64_t)n * nib_row + (int64_t)row0 * sc_row, (uint32_t)(nrows * sc_row));
+  const auto xr = make_rsrc(x, (uint32_t)k * 2u);
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+  for (int ch = kwi; ch < kc; ch += kw) {
+    const int e0 = ch * 2048 + 32 * lane;
+    const bool valid = e0 < k;
+    u32x4 nib[R];
+    unsigned sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      nib[r] = ld128(nr, (uint32_t)(r * nib_row + ch * 1024 + 16 * lane));
+      sc[r] = ld16(sr, (uint32_t)(r * sc_row + ch * 128 + 2 * lane));
+    }
+    unsigned X[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = ld128(xr, (uint32_t)e0 * 2u + 16u * i);
+      X[4 * i] = v.x; X[4 * i + 1] = v.y; X[4 * i + 2] = v.z; X[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const unsigned q[4] = {nib[r].x, nib[r].y, nib[r].z, nib[r].w};
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x2 p0 = fp4x2_bf16(q[j >> 2], j);
+        a0 = dot2bf(p0, X[j], a0);
+        const bf16x2 p1 = fp4x2_bf16(q[2 + (j >> 2)], j);
+        a1 = dot2bf(p1, X[8 + j], a1);
+      }
+      const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc[r], 0));
+      const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc[r], 1));
+      const float part = __builtin_fmaf(s1, a1, s0 * a0);
+      acc[r] += valid ? part : 0.f;
+    }
+  }
+
+  wave_reduce_rows<R>(acc);
+  constexpr int L = log2i<R>();
+  constexpr int kLanesPerRow = 64 >> L;
+  if ((lane & (kLanesPerRow - 1)) == 0)
+    red[(rgi * kw + kwi) * R + (lane >> (6 - L))] = acc[0];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < rg * R) {
+    const int g = t / R, r = t % R;
+    float s = 0.f;
+    for (int kk = 0; kk < kw; ++kk) s += red[(g * kw + kk) * R + r];
+    const int row = blockIdx.x * rg * R + g * R + r;
+    if (row < n) y[row] = s;
+  }
+}
+
+// One thread per 16 nibble bytes = 32 weights = two scale blocks.  The
+// flattened [M][K] index of a weight is twice its nibble-byte index (plus the
+// nibble), and its scale is byte (flattened index)/16 of the scale array,
+// because K is a multiple of 32.
+__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t* __restrict__ w,
+                                                            float* __restrict__ out,
+                                                            int64_t n_by_k) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t * 32 >= n_by_k) return;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(w + 16 * t);
+  const unsigned sc = *reinterpret_cast<const uint16_t*>(w + n_by_k / 2 + 2 * t);
+  const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 0));
+  const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 1));
+  const unsigned q[4] = {v.x, v.y, v.z, v.w};
+  float o[32];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const f32x2 e = fp4x2_f32(q[j >> 2], j);
+    const float s = j < 8 ? s0 : s1;
+    o[2 * j] = e.x * s;
+    o[2 * j + 1] = e.y * s;
+  }
+  float* dst = out + 32 * t;
+#pragma unroll
+  for (int j = 0; j < 32; j += 4)
+    *reinterpret_cast<float4*>(dst + j) = make_float4(o[j], o[j + 1], o[j + 2], o[j + 3]);
+}
+
+template <int R>
+static hipError_t launch_nvfp4_r(const void* w, const void* x, float* y, int64_t n, int64_t k,
+                                 hipStream_t s) {
+  const int kc = (int)((k + 2047) / 2048);
+  const int kw = kc < 8 ? kc : 8;
+  const int rg = kw >= 8 ? 1 : 8 / kw;
+  const int rows_per_wg = rg * R;
+  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(nvfp4_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)k, kc, kw, rg);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
+                             hipStream_t s) {
+  return launch_nvfp4_r<8>(w, x, y, n, k, s);
+}
+
+hipError_t launch_nvfp4_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
+  const int64_t threads = n * k / 32;
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     (const uint8_t*)w, out, n * k);
+  return hipGetLastError();
+}
+
+}  // namespace qgemv

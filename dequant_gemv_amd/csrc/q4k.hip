@@ -1,0 +1,223 @@
+// Q4_K fused dequantise + GEMV and fp32 dequantise for gfx950.
+//
+// Block format ("Writing a high performant GEMV + dequant for Metal", sections
+// "What is a weight block?" and "Kernel code"): 144 bytes per 256 weights,
+// fp16 d @0, fp16 dmin @2, 12 bytes of 6-bit scales/mins @4, 128 nibble bytes
+// @16.  Weight i = d*s_g*q_i - dmin*m_g, g = i/32 (section "Compute").
+//
+// GEMV work split.  A wave owns one K-chunk of 8 blocks (2048 weights) for R
+// consecutive rows.  Lane l takes block l/8 of the chunk and the 16-byte slice
+// p = l%8 of its nibbles, so one dwordx4 per lane reads the 128 contiguous
+// nibble bytes of 8 blocks: every load instruction is one contiguous 1 KiB run
+// with 16-byte gaps, i.e. coalesced.  Nibble byte 16p+j sits at element
+// 64c+16h+j (low nibble, group 2c) and 64c+32+16h+j (high nibble, group 2c+1)
+// with c = p/2, h = p%2, so a lane touches exactly two groups per block.
+//
+// The dot product uses the page's factoring (section "Compute"): per group
+// d*s_g*Q_g - dmin*m_g*X_g with Q_g = sum x_i q_i and X_g = sum x_i.  X_g over
+// the lane's 16 elements is computed once per chunk and reused by all R rows,
+// as are the lane's 32 activations, held in registers as fp16 pairs.  Q_g is
+// built with v_dot2_f32_f16 straight on masked nibbles: a nibble masked in
+// place is an fp16 subnormal q*2^-24 (low nibble) or 16q*2^-24 (high nibble),
+// so no shift or integer->float conversion is spent per weight; the power of
+// two is removed once per row (the shift-deferral of the page's Figures 7-8
+// carried to the fp16 bit level).  Products are exact in fp32.
+//
+// Per row the lane's partial is reduced across the wave (R rows at once, see
+// wave_reduce_rows) and across the K-chunk waves through LDS.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qgemv {
+
+constexpr int kQ4kBytes = 144;
+
+// 6-bit scale and min of the two consecutive groups (2c, 2c+1) a lane owns,
+// packed as bytes 0 and 1.  h1, h2, h3 are scale bytes 0-3, 4-7, 8-11.  Groups
+// 0-3 keep their 6 bits in the low bits of bytes 0-7; groups 4-7 take the low
+// (scale) or high (min) nibble of bytes 8-11 and the top two bits of bytes
+// 0-3 (scale) or 4-7 (min).
+struct Q4kScaleSel {
+  unsigned sh, shm, ma, mb;
+  bool hi;
+  __device__ __forceinline__ explicit Q4kScaleSel(int c) {
+    hi = c >= 2;
+    sh = 16u * (unsigned)(c & 1);
+    shm = sh + (hi ? 4u : 0u);
+    ma = hi ? 0x0F0Fu : 0x3F3Fu;
+    mb = hi ? 0x3030u : 0u;
+  }
+  __device__ __forceinline__ unsigned scales(unsigned h1, unsigned h3) const {
+    unsigned a = hi ? h3 : h1;
+    return ((a >> sh) & ma) | ((h1 >> (sh + 2)) & mb);
+  }
+  __device__ __forceinline__ unsigned mins(unsigned h2, unsigned h3) const {
+    unsigned a = hi ? h3 : h2;
+    return ((a >> shm) & ma) | ((h2 >> (sh + 2)) & mb);
+  }
+};
+
+template <int R>
+__global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict__ w,
+                                                       const uint16_t* __restrict__ x,
+                                                       float* __restrict__ y, int n, int nb,
+                                                       int kc, int kw, int rg) {
+  __shared__ float red[16 * 16];
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int kwi = wave % kw;
+  const int rgi = wave / kw;
+  const int64_t row_bytes = (int64_t)nb * kQ4kBytes;
+  const int row0 = blockIdx.x * rg * R + rgi * R;
+  const int nrows = max(0, min(R, n - row0));
+  const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, (uint32_t)(nrows * row_bytes));
+  const auto xr = make_rsrc(x, (uint32_t)nb * 512u);
+
+  const int bl = lane >> 3, p = lane & 7, c = p >> 1, h = p & 1;
+  const Q4kScaleSel sel(c);
+  const unsigned kOnes = 0x3C003C00u;  // fp16 (1, 1)
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+  for (int ch = kwi; ch < kc; ch += kw) {
+    const int b = ch * 8 + bl;
+    const bool valid = b < nb;
+    // Issue the weight loads of all R rows first: they are the long pole.
+    u32x4 hdr[R], qs[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t off = (uint32_t)(r * row_bytes + b * kQ4kBytes);
+      hdr[r] = ld128(wr, off);
+      qs[r] = ld128(wr, off + 16 + 16 * p);
+    }
+    // The lane's 32 activations: 16 of group 2c and 16 of group 2c+1.
+    const uint32_t xo = (uint32_t)(b * 256 + 64 * c + 16 * h) * 2u;
+    const u32x4 xa0 = ld128(xr, xo), xa1 = ld128(xr, xo + 16);
+    const u32x4 xb0 = ld128(xr, xo + 64), xb1 = ld128(xr, xo + 80);
+    const unsigned XA[8] = {xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
+    const unsigned XB[8] = {xb0.x, xb0.y, xb0.z, xb0.w, xb1.x, xb1.y, xb1.z, xb1.w};
+    // Pairs (x[4t], x[4t+2]) and (x[4t+1], x[4t+3]) match the two fp16 halves
+    // of a nibble dword masked with 0x000F000F / 0x00F000F0 (bytes 0 and 2)
+    // and the same after >> 8 (bytes 1 and 3).
+    unsigned pa02[4], pa13[4], pb02[4], pb13[4];
+    float sxa = 0.f, sxb = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pa02[t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x05040100u);
+      pa13[t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x07060302u);
+      pb02[t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x05040100u);
+      pb13[t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x07060302u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sxa = dot2h(XA[i], kOnes, sxa);
+      sxb = dot2h(XB[i], kOnes, sxb);
+    }
+    // X_g * 2^-24, to meet Q_g * 2^-24 from the subnormal nibbles.
+    sxa *= 0x1p-24f;
+    sxb *= 0x1p-24f;
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const unsigned q[4] = {qs[r].x, qs[r].y, qs[r].z, qs[r].w};
+      float qa = 0.f, qb = 0.f;  // 2^-24 Q_a, 2^-20 Q_b
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const unsigned w0 = q[t], w8 = q[t] >> 8;
+        qa = dot2h(w0 & 0x000F000Fu, pa02[t], qa);
+        qa = dot2h(w8 & 0x000F000Fu, pa13[t], qa);
+        qb = dot2h(w0 & 0x00F000F0u, pb02[t], qb);
+        qb = dot2h(w8 & 0x00F000F0u, pb13[t], qb);
+      }
+      const unsigned sp = sel.scales(hdr[r].y, hdr[r].w);
+      const unsigned mp = sel.mins(hdr[r].z, hdr[r].w);
+      const float sa = (float)(sp & 0xFFu), sb = (float)((sp >> 8) & 0xFFu);
+      const float ma = (float)(mp & 0xFFu), mb = (float)((mp >> 8) & 0xFFu);
+      const float d = f16lo(hdr[r].x), dmin = f16hi(hdr[r].x);
+      const float v = __builtin_fmaf(sb, qb * 0.0625f, sa * qa);
+      const float mx = __builtin_fmaf(mb, sxb, ma * sxa);
+      const float part = __builtin_fmaf(d, v, -dmin * mx);
+      acc[r] += valid ? part : 0.f;
+    }
+  }
+
+  wave_reduce_rows<R>(acc);
+  constexpr int L = log2i<R>();
+  constexpr int kLanesPerRow = 64 >> L;
+  if ((lane & (kLanesPerRow - 1)) == 0)
+    red[(rgi * kw + kwi) * R + (lane >> (6 - L))] = acc[0];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < rg * R) {
+    const int g = t / R, r = t % R;
+    float s = 0.f;
+    for (int k = 0; k < kw; ++k) s += red[(g * kw + k) * R + r];
+    const int row = blockIdx.x * rg * R + g * R + r;
+    if (row < n) y[row] = s * 0x1p24f;
+  }
+}
+
+// One thread per (block, 16-byte nibble slice): 32 weights, written as the
+// correctly rounded fp32 of d*s*q - dmin*m (both products are exact in fp32,
+// so one fma rounds once).
+__global__ __launch_bounds__(256) void q4k_dequant_kernel(const uint8_t* __restrict__ w,
+                                                          float* __restrict__ out,
+                                                          int64_t nblocks) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= nblocks * 8) return;
+  const int64_t g = gid >> 3;
+  const int p = (int)(gid & 7), c = p >> 1, h = p & 1;
+  const u32x4 hdr = *reinterpret_cast<const u32x4*>(w + g * kQ4kBytes);
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(w + g * kQ4kBytes + 16 + 16 * p);
+  const Q4kScaleSel sel(c);
+  const unsigned sp = sel.scales(hdr.y, hdr.w), mp = sel.mins(hdr.z, hdr.w);
+  const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
+  const float dsa = d * (float)(sp & 0xFFu), dsb = d * (float)((sp >> 8) & 0xFFu);
+  const float dma = dmin * (float)(mp & 0xFFu), dmb = dmin * (float)((mp >> 8) & 0xFFu);
+  const unsigned q[4] = {qv.x, qv.y, qv.z, qv.w};
+  float lo[16], hi[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const unsigned byte = (q[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    lo[j] = __builtin_fmaf(dsa, (float)(byte & 15u), -dma);
+    hi[j] = __builtin_fmaf(dsb, (float)(byte >> 4), -dmb);
+  }
+  float* o = out + g * 256 + 64 * c + 16 * h;
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    *reinterpret_cast<float4*>(o + j) = make_float4(lo[j], lo[j + 1], lo[j + 2], lo[j + 3]);
+    *reinterpret_cast<float4*>(o + 32 + j) = make_float4(hi[j], hi[j + 1], hi[j + 2], hi[j + 3]);
+  }
+}
+
+template <int R>
+static hipError_t launch_q4k_r(const void* w, const void* x, float* y, int64_t n, int64_t k,
+                               hipStream_t s) {
+  const int nb = (int)(k / 256);
+  const int kc = (nb + 7) / 8;
+  const int kw = kc < 8 ? kc : 8;
+  const int rg = kw >= 8 ? 1 : 8 / kw;
+  const int rows_per_wg = rg * R;
+  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(q4k_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, nb, kc, kw, rg);
+  return hipGetLastError();
+}
+
+hipError_t launch_q4k_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
+                           hipStream_t s) {
+  return launch_q4k_r<8>(w, x, y, n, k, s);
+}
+
+hipError_t launch_q4k_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
+  const int64_t nblocks = n * (k / 256);
+  const int64_t threads = nblocks * 8;
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(q4k_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     (const uint8_t*)w, out, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace qgemv

@@ -1,0 +1,239 @@
+// TQ1_0 fused dequantise + GEMV and fp32 dequantise for gfx950.
+//
+// Format ("metal: TQ1_0 kernel performance", sections 1 and 2): 54 bytes per
+// 256 weights, qs[48] (five base-3 digits per byte) | qh[4] (four digits per
+// byte) | fp16 d.  Digit k of byte b is floor(3^(k+1) b / 256) - 3 floor(3^k b / 256);
+// digit k of qs[j] feeds element 32k+j (j < 32) or 160+16k+(j-32) (j < 48),
+// digit k < 4 of qh[m] feeds element 240+4k+m; weight = d*(digit-1).
+//
+// GEMV work split.  That page's flattened mat-vec treats qs and qh as one
+// 52-byte payload; here the whole row is the payload stream.  A wave owns a
+// segment of 16 blocks (864 bytes = 54 dwordx4, lanes 0..53, coalesced) for R
+// rows.  Every byte pair (2i, 2i+1) of a lane's 16 bytes belongs to one block
+// (blocks start at even offsets) and its two bytes feed activation pairs that
+// are adjacent in x (elements e, e+1 for the same digit), so each lane keeps
+// 8 pairs x 5 digits of fp16 activation pairs in registers, loaded once per
+// segment; coefficients of non-elements (digit 4 of qh bytes, the d bytes)
+// are zero, the zero-padding trick of the page's section 1, so all byte pairs
+// run one code path.
+//
+// Digits in registers: with B = (b0 | b1 << 16) and packed 16-bit arithmetic
+// (wrapping mod 2^16), F_k = (B * 4 * 3^k) & 0xFC00 = floor(3^k b / 256) << 10
+// (mod 2^16), and F_{k+1} - 3 F_k = digit_k << 10 exactly.  The 16-bit pattern
+// digit << 10 is the fp16 number digit * 2^-14 (0, 2^-14 or 2^-13, all normal
+// or zero), so v_dot2_f32_f16 consumes it directly against the activation pair:
+// sum x*t = 2^14 * acc exactly up to fp32 accumulation.  No fp16 arithmetic
+// touches the digits themselves (the page's "Not applicable" section shows why
+// fp16 floors fail).
+//
+// Each block's d sits in the lane whose 16 bytes hold bytes 52-53 of that
+// block; lanes fetch the d of the (at most two) blocks they touch with
+// ds_bpermute.  sum x*(t-1) = sum x*t - sum x, the second term precomputed.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qgemv {
+
+constexpr int kTq1Bytes = 54;
+constexpr int kTq1SegBlocks = 16;
+constexpr int kTq1SegBytes = kTq1SegBlocks * kTq1Bytes;  // 864 = 54 * 16
+
+// Element (0..255) fed by digit k of payload byte pos, or -1.
+__device__ __forceinline__ int tq1_element(int pos, int k) {
+  if (pos < 32) return 32 * k + pos;
+  if (pos < 48) return 160 + 16 * k + (pos - 32);
+  if (pos < 52) return k < 4 ? 240 + 4 * k + (pos - 48) : -1;
+  return -1;
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16v2;
+
+__device__ __forceinline__ u16v2 as_u16v2(unsigned v) { return __builtin_bit_cast(u16v2, v); }
+__device__ __forceinline__ unsigned as_u32(u16v2 v) { return __builtin_bit_cast(unsigned, v); }
+
+// Five fp16 pairs (digit_k(b0) * 2^-14, digit_k(b1) * 2^-14), k = 0..4.
+__device__ __forceinline__ void tq1_digits(unsigned B, unsigned (&D)[5]) {
+  const u16v2 b = as_u16v2(B);
+  const u16v2 m = {0xFC00, 0xFC00};
+  u16v2 F[6];
+#pragma unroll
+  for (int k = 1; k <= 5; ++k) {
+    const unsigned short c = (unsigned short)(4 * (k == 1 ? 3 : k == 2 ? 9 : k == 3 ? 27 : k == 4 ? 81 : 243));
+    F[k] = (b * (u16v2){c, c}) & m;
+  }
+  D[0] = as_u32(F[1]);
+#pragma unroll
+  for (int k = 1; k <= 4; ++k) D[k] = as_u32(F[k + 1] + F[k] * (u16v2){0xFFFD, 0xFFFD});
+}
+
+template <int R>
+__global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict__ w,
+                                                       const uint16_t* __restrict__ x,
+                                                       float* __restrict__ y, int n, int nb,
+                                                       int kc, int kw, int rg) {
+  __shared__ float red[16 * 16];
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int kwi = wave % kw;
+  const int rgi = wave / kw;
+  const int64_t row_bytes = (int64_t)nb * kTq1Bytes;
+  const int row0 = blockIdx.x * rg * R + rgi * R;
+  const int nrows = max(0, min(R, n - row0));
+  const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, (uint32_t)(nrows * row_bytes));
+  const auto xr = make_rsrc(x, (uint32_t)nb * 512u);
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+  const int o0 = 16 * lane;  // first byte of this lane inside a segment
+  const int blk_first = o0 / kTq1Bytes;
+
+  for (int ch = kwi; ch < kc; ch += kw) {
+    const int nbs = min(kTq1SegBlocks, nb - ch * kTq1SegBlocks);  // blocks in this segment
+    const bool active = lane < 54 && blk_first < nbs;
+    u32x4 raw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      raw[r] = ld128(wr, (uint32_t)(r * row_bytes + ch * kTq1SegBytes + o0));
+
+    // Per-lane activation pairs for 8 byte pairs x 5 digits, zero where the
+    // digit feeds no element of a block inside this segment.
+    unsigned xp[8][5];
+    float xs0 = 0.f, xs1 = 0.f;  // sum of x over the lane's elements, per slot
+    int bnd = 8;                 // byte pairs in the lane's first block
+    const unsigned kOnes = 0x3C003C00u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = o0 + 2 * i;
+      const int blk = o / kTq1Bytes;
+      const int pos = o - blk * kTq1Bytes;
+      const bool in = active && blk < nbs;
+      if (blk != blk_first && bnd == 8) bnd = i;
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        const int e = tq1_element(pos, k);
+        const int ge = (ch * kTq1SegBlocks + blk) * 256 + e;
+        const unsigned v = ld32(xr, (uint32_t)ge * 2u);
+        xp[i][k] = (in && e >= 0) ? v : 0u;
+        if (blk == blk_first) xs0 = dot2h(xp[i][k], kOnes, xs0);
+        else xs1 = dot2h(xp[i][k], kOnes, xs1);
+      }
+    }
+    // Which lane holds d of the blocks this lane touches, and where this
+    // lane's own d (if any) sits inside its 16 bytes.
+    int hold_off = -1;
+    for (int bh = blk_first; bh <= blk_first + 1; ++bh) {
+      const int dpos = bh * kTq1Bytes + 52 - o0;
+      if (dpos >= 0 && dpos < 16) hold_off = dpos;
+    }
+    const int src0 = ((blk_first * kTq1Bytes + 52) / 16) << 2;
+    const int src1 = (((blk_first + 1) * kTq1Bytes + 52) / 16) << 2;
+    const bool slot0 = active;
+    const bool slot1 = active && bnd < 8 && blk_first + 1 < nbs;
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const unsigned dw[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+      // d held by this lane (0 if none)
+      unsigned hw = dw[0];
+      hw = (hold_off >> 2) == 1 ? dw[1] : hw;
+      hw = (hold_off >> 2) == 2 ? dw[2] : hw;
+      hw = (hold_off >> 2) == 3 ? dw[3] : hw;
+      const float dh = hold_off < 0 ? 0.f : ((hold_off & 2) ? f16hi(hw) : f16lo(hw));
+      const float d0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src0, __builtin_bit_cast(int, dh)));
+      const float d1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src1, __builtin_bit_cast(int, dh)));
+
+      float a = 0.f, snap = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned B = __builtin_amdgcn_perm(0u, dw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
+        unsigned D[5];
+        tq1_digits(B, D);
+#pragma unroll
+        for (int k = 0; k < 5; ++k) a = dot2h(D[k], xp[i][k], a);
+        snap = (i == bnd - 1) ? a : snap;
+      }
+      const float p0 = d0 * __builtin_fmaf(snap, 16384.f, -xs0);
+      const float p1 = d1 * __builtin_fmaf(a - snap, 16384.f, -xs1);
+      acc[r] += (slot0 ? p0 : 0.f) + (slot1 ? p1 : 0.f);
+    }
+  }
+
+  wave_reduce_rows<R>(acc);
+  constexpr int L = log2i<R>();
+  constexpr int kLanesPerRow = 64 >> L;
+  if ((lane & (kLanesPerRow - 1)) == 0)
+    red[(rgi * kw + kwi) * R + (lane >> (6 - L))] = acc[0];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < rg * R) {
+    const int g = t / R, r = t % R;
+    float s = 0.f;
+    for (int kk = 0; kk < kw; ++kk) s += red[(g * kw + kk) * R + r];
+    const int row = blockIdx.x * rg * R + g * R + r;
+    if (row < n) y[row] = s;
+  }
+}
+
+// One thread per (block, run of 16 elements il): elements 16 il .. 16 il + 15.
+// For il < 10 they are digit il/2 of qs[16 (il%2) + e]; for il < 15 digit
+// il-10 of qs[32 + e]; il = 15 is digit e/4 of qh[e%4] (the section-2 element
+// order of the TQ1_0 page).  Weight = d * (digit - 1), exact in fp32.
+__global__ __launch_bounds__(256) void tq1_dequant_kernel(const uint8_t* __restrict__ w,
+                                                          float* __restrict__ out,
+                                                          int64_t nblocks) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nblocks * 16) return;
+  const int64_t g = t >> 4;
+  const int il = (int)(t & 15);
+  const uint8_t* b = w + g * kTq1Bytes;
+  const float d = (float)__builtin_bit_cast(_Float16, (unsigned short)(b[52] | (b[53] << 8)));
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    int byte, k;
+    if (il < 10) { byte = 16 * (il & 1) + e; k = il >> 1; }
+    else if (il < 15) { byte = 32 + e; k = il - 10; }
+    else { byte = 48 + (e & 3); k = e >> 2; }
+    int p = 1;
+    for (int j = 0; j < k; ++j) p *= 3;
+    const int v = b[byte];
+    const int digit = (p * 3 * v) / 256 - 3 * ((p * v) / 256);
+    o[e] = d * (float)(digit - 1);
+  }
+  float* dst = out + g * 256 + 16 * il;
+#pragma unroll
+  for (int e = 0; e < 16; e += 4)
+    *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+}
+
+template <int R>
+static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n, int64_t k,
+                               hipStream_t s) {
+  const int nb = (int)(k / 256);
+  const int kc = (nb + kTq1SegBlocks - 1) / kTq1SegBlocks;
+  const int kw = kc < 8 ? kc : 8;
+  const int rg = kw >= 8 ? 1 : 8 / kw;
+  const int rows_per_wg = rg * R;
+  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(tq1_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, nb, kc, kw, rg);
+  return hipGetLastError();
+}
+
+hipError_t launch_tq1_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
+                           hipStream_t s) {
+  return launch_tq1_r<4>(w, x, y, n, k, s);
+}
+
+hipError_t launch_tq1_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
+  const int64_t nblocks = n * (k / 256);
+  const int64_t threads = nblocks * 16;
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(tq1_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     (const uint8_t*)w, out, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace qgemv

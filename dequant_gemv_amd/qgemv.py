@@ -1,0 +1,173 @@
+"""Thin ctypes binding of libqgemv (include/qgemv.h).
+
+Same names as the C entry points; the functions only turn torch tensors (or
+raw device addresses) into pointers and the current HIP stream, call the
+library and raise on a non-zero return code.  Every step of the computation
+runs in the library's HIP kernels; there is no fallback path: if the library
+is missing this module fails at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+QGEMV_OK = 0
+QGEMV_E_NULL = -1
+QGEMV_E_SHAPE = -2
+QGEMV_E_ALIGN = -3
+QGEMV_E_HIP = -4
+QGEMV_E_ALIAS = -5
+
+# Entry points declared in include/qgemv.h.
+GEMV_SYMBOLS = ("qgemv_q4k", "qgemv_nvfp4", "qgemv_tq1")
+DEQUANT_SYMBOLS = ("qdequant_q4k", "qdequant_nvfp4", "qdequant_tq1")
+ALL_SYMBOLS = GEMV_SYMBOLS + DEQUANT_SYMBOLS + (
+    "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror", "qgemv_last_hip_error",
+    "qgemv_build_id")
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.qgemv_strerror(code).decode()
+        if code == QGEMV_E_HIP:
+            msg += f" (hipError {_lib.qgemv_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{code}]")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    for name in GEMV_SYMBOLS:
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, P, I64, I64, P]
+    for name in DEQUANT_SYMBOLS:
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, I64, I64, P]
+    lib.qgemv_read_ceiling.restype = ctypes.c_int
+    lib.qgemv_read_ceiling.argtypes = [P, I64, P, P]
+    lib.qgemv_read_sink_len.restype = ctypes.c_int64
+    lib.qgemv_read_sink_len.argtypes = [I64]
+    lib.qgemv_strerror.restype = ctypes.c_char_p
+    lib.qgemv_strerror.argtypes = [ctypes.c_int]
+    lib.qgemv_last_hip_error.restype = ctypes.c_int
+    lib.qgemv_build_id.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _addr(t) -> int:
+    """Device address of a torch tensor (must live on the GPU), or an int."""
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("qgemv takes device memory: move the tensor to the GPU first")
+    if not t.is_contiguous():
+        raise ValueError("qgemv takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != QGEMV_OK:
+        raise QgemvError(rc, where)
+
+
+def _gemv(name, w, x, y, M, K, stream):
+    _check(getattr(_lib, name)(_addr(w), _addr(x), _addr(y), int(M), int(K), _stream(stream)), name)
+    return y
+
+
+def qgemv_q4k(w, x, y, M, K, stream=None):
+    """y[M] (fp32) = x[K] (fp16) . dequant_Q4_K(w)^T, enqueued on `stream`."""
+    return _gemv("qgemv_q4k", w, x, y, M, K, stream)
+
+
+def qgemv_nvfp4(w, x, y, M, K, stream=None):
+    """y[M] (fp32) = x[K] (bf16) . dequant_NVFP4(w)^T, enqueued on `stream`."""
+    return _gemv("qgemv_nvfp4", w, x, y, M, K, stream)
+
+
+def qgemv_tq1(w, x, y, M, K, stream=None):
+    """y[M] (fp32) = x[K] (fp16) . dequant_TQ1_0(w)^T, enqueued on `stream`."""
+    return _gemv("qgemv_tq1", w, x, y, M, K, stream)
+
+
+def _dequant(name, w, out, M, K, stream):
+    _check(getattr(_lib, name)(_addr(w), _addr(out), int(M), int(K), _stream(stream)), name)
+    return out
+
+
+def qdequant_q4k(w, out, M, K, stream=None):
+    return _dequant("qdequant_q4k", w, out, M, K, stream)
+
+
+def qdequant_nvfp4(w, out, M, K, stream=None):
+    return _dequant("qdequant_nvfp4", w, out, M, K, stream)
+
+
+def qdequant_tq1(w, out, M, K, stream=None):
+    return _dequant("qdequant_tq1", w, out, M, K, stream)
+
+
+def qgemv_read_sink_len(nbytes: int) -> int:
+    return int(_lib.qgemv_read_sink_len(int(nbytes)))
+
+
+def qgemv_read_ceiling(buf, nbytes, sink, stream=None):
+    _check(_lib.qgemv_read_ceiling(_addr(buf), int(nbytes), _addr(sink), _stream(stream)),
+           "qgemv_read_ceiling")
+    return sink
+
+
+def qgemv_build_id() -> str:
+    return _lib.qgemv_build_id().decode()
+
+
+def qgemv_strerror(code: int) -> str:
+    return _lib.qgemv_strerror(int(code)).decode()
+
+
+# Convenience: allocate y / out with torch and dispatch by format name.
+GEMV = {"q4k": qgemv_q4k, "nvfp4": qgemv_nvfp4, "tq1": qgemv_tq1}
+DEQUANT = {"q4k": qdequant_q4k, "nvfp4": qdequant_nvfp4, "tq1": qdequant_tq1}
+
+
+def gemv(fmt: str, w, x, M: int, K: int, y=None, stream=None):
+    import torch
+
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=w.device)
+    return GEMV[fmt](w, x, y, M, K, stream)
+
+
+def dequant(fmt: str, w, M: int, K: int, out=None, stream=None):
+    import torch
+
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=w.device)
+    return DEQUANT[fmt](w, out, M, K, stream)

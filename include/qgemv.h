@@ -1,0 +1,108 @@
+/*
+ * qgemv.h — C ABI of the MI355X (gfx950) fused dequantise + GEMV library.
+ *
+ * Every call computes, for ONE activation row,
+ *     y[r] = sum_{i<K} x[i] * dequant(W)[r][i]        r = 0 .. M-1
+ * i.e. y = x . dequant(W)^T with alpha = 1 and beta = 0 ("Writing a high
+ * performant GEMV + dequant for Metal", section "What is a GEMV"), or
+ * materialises dequant(W) as fp32.
+ *
+ * Conventions shared by every entry point
+ *   M       number of rows of W = number of outputs (the batch is always 1).
+ *   K       reduction length (elements per row of W and of x).
+ *   Layout  W is row-major with K contiguous, in the format's packed blocks;
+ *           x is K contiguous 16-bit values; y is M contiguous fp32 values;
+ *           dequant outputs are M*K contiguous fp32 values, row-major.
+ *   Memory  every pointer is DEVICE memory owned by the caller (e.g. torch
+ *           tensors).  The library allocates nothing, keeps no per-call state
+ *           and never synchronises.  y must not overlap x or W.
+ *   Stream  work is enqueued on `stream` (NULL = the null stream) and returns
+ *           immediately; results are visible once the stream has run it.
+ *   Errors  arguments are validated in host code before any HIP call; a bad
+ *           argument returns a negative QGEMV_E_* code and enqueues nothing.
+ *           A failed launch returns QGEMV_E_HIP.  The library never prints or
+ *           aborts.  M == 0 is a successful no-op.
+ *   Alignment  W, x and dequant outputs must be 16-byte aligned; y 4-byte.
+ *   Threads    calls are thread-safe (no global mutable state).
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t *` */
+
+enum {
+  QGEMV_OK = 0,
+  QGEMV_E_NULL = -1,  /* a required pointer is NULL (with M > 0) */
+  QGEMV_E_SHAPE = -2, /* M < 0, K <= 0, K not a multiple of the block, or sizes overflow */
+  QGEMV_E_ALIGN = -3, /* a pointer is not aligned as required */
+  QGEMV_E_HIP = -4,   /* the HIP runtime rejected the launch */
+  QGEMV_E_ALIAS = -5  /* the output overlaps an input */
+};
+
+/* Q4_K ("Writing a high performant GEMV + dequant for Metal", sections "What is
+ * a weight block?", "Compute", "Kernel code"): K % 256 == 0; each row holds K/256
+ * super-blocks of 144 bytes: fp16 d @0, fp16 dmin @2, 12 bytes of packed 6-bit
+ * group scales/mins @4, 128 bytes of 4-bit quants @16 (little-endian).  Weight i
+ * of a block is d*s_g*q_i - dmin*m_g with g = i/32.  x is fp16.
+ * W occupies M*(K/256)*144 bytes. */
+int qgemv_q4k(const void* w, const void* x_f16, float* y, int64_t M, int64_t K,
+              struct ihipStream_t* stream);
+
+/* NVFP4 W4A16 (Mojo module "fp4_gemv", function enqueue_apple_fp4_gemv: out =
+ * a @ dequant(packed, scales)^T at M = 1): K % 32 == 0.  W is ONE buffer of
+ * M*K/2 bytes of E2M1 nibbles ([M][K/2], the even element in the low nibble)
+ * followed, at byte offset M*K/2, by M*K/16 OCP FP8 E4M3 scale bytes ([M][K/16],
+ * one per 16 consecutive weights of a row).  Weight = e2m1 * |scale|.  x is bf16.
+ * W occupies M*K/2 + M*K/16 bytes. */
+int qgemv_nvfp4(const void* w, const void* x_bf16, float* y, int64_t M, int64_t K,
+                struct ihipStream_t* stream);
+
+/* TQ1_0 ("metal: TQ1_0 kernel performance", sections 1 and 2): K % 256 == 0;
+ * each row holds K/256 blocks of 54 bytes: qs[48] @0 (five base-3 digits per
+ * byte), qh[4] @48 (four digits per byte), fp16 d @52.  Digit k of byte b is
+ * floor(3*((3^k*b) mod 256)/256); digit k of qs[j] feeds element 32k+j (j<32)
+ * or 160+16(k)+(j-32) (32<=j<48); digit k<4 of qh[m] feeds element 240+4k+m.
+ * Weight = d*(digit-1).  x is fp16.  W occupies M*(K/256)*54 bytes. */
+int qgemv_tq1(const void* w, const void* x_f16, float* y, int64_t M, int64_t K,
+              struct ihipStream_t* stream);
+
+/* fp32 materialisation out[M][K] of the same formats (same W conventions as
+ * above).  Each value is the correctly rounded fp32 of the exact weight, which
+ * for these formats is the exact weight itself whenever it is representable
+ * (the bit-exact reference for the GEMVs; Mojo module "fp4_gemv", TQ1_0 PR
+ * section "Correctness"). */
+int qdequant_q4k(const void* w, float* out, int64_t M, int64_t K, struct ihipStream_t* stream);
+int qdequant_nvfp4(const void* w, float* out, int64_t M, int64_t K, struct ihipStream_t* stream);
+int qdequant_tq1(const void* w, float* out, int64_t M, int64_t K, struct ihipStream_t* stream);
+
+/* Bandwidth ceiling probe: streams `bytes` bytes of device memory at `buf`
+ * (16-byte aligned, bytes % 16 == 0) with the same dwordx4 loads the GEMVs use
+ * and writes one fp32 per workgroup into `sink` (at least qgemv_read_sink_len(bytes)
+ * floats) so the loads cannot be elided.  The practical roofline of the part
+ * ("Writing a high performant GEMV + dequant for Metal", section "Roofline
+ * Analysis": a memory-bound kernel is limited by the DRAM bandwidth). */
+int qgemv_read_ceiling(const void* buf, int64_t bytes, float* sink, struct ihipStream_t* stream);
+int64_t qgemv_read_sink_len(int64_t bytes);
+
+/* Human-readable text of a QGEMV_* code (static storage). */
+const char* qgemv_strerror(int code);
+
+/* HIP error code of the last launch failure on the calling thread (0 if none). */
+int qgemv_last_hip_error(void);
+
+/* Provenance: hash of the sources this library was built from ("metal: TQ1_0
+ * kernel performance", section "Measuring this yourself": confirm which build
+ * is being measured immediately before measuring). */
+const char* qgemv_build_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

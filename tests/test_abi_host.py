@@ -1,0 +1,101 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/qgemv.h declares, carries the build id of its sources, and rejects bad
+arguments in host code (these calls return before any HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    from dequant_gemv_amd import qgemv
+
+    return qgemv
+
+
+def test_header_symbols_exported(q):
+    names = _header_functions()
+    assert len(names) == 11, names
+    lib = q.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(q.ALL_SYMBOLS) == names
+
+
+def test_build_id_matches_sources(q):
+    from dequant_gemv_amd import build
+
+    assert q.qgemv_build_id() == build.build_id()
+
+
+def test_strerror(q):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert q.qgemv_strerror(code)
+    assert "unknown" in q.qgemv_strerror(42)
+
+
+A = 0x7F0000000000  # a 16-byte aligned fake device address, never dereferenced
+
+
+@pytest.mark.parametrize("name,kmul", [("qgemv_q4k", 256), ("qgemv_nvfp4", 32), ("qgemv_tq1", 256)])
+def test_gemv_validation(q, name, kmul):
+    f = getattr(q.lib(), name)
+    W, X, Y = A, A + (1 << 32), A + (2 << 32)
+    assert f(W, X, Y, -1, kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 4, 0, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 4, kmul + 16, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 4, -kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 4, (1 << 24) + kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 1 << 31, kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 0, kmul, None) == q.QGEMV_OK  # empty: no-op, no launch
+    assert f(None, X, Y, 4, kmul, None) == q.QGEMV_E_NULL
+    assert f(W, None, Y, 4, kmul, None) == q.QGEMV_E_NULL
+    assert f(W, X, None, 4, kmul, None) == q.QGEMV_E_NULL
+    assert f(W + 8, X, Y, 4, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, X + 2, Y, 4, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, X, Y + 2, 4, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, X, W + 16, 4, kmul, None) == q.QGEMV_E_ALIAS
+    assert f(W, X, X, 4, kmul, None) == q.QGEMV_E_ALIAS
+
+
+@pytest.mark.parametrize("name,kmul", [("qdequant_q4k", 256), ("qdequant_nvfp4", 32), ("qdequant_tq1", 256)])
+def test_dequant_validation(q, name, kmul):
+    f = getattr(q.lib(), name)
+    W, O = A, A + (1 << 36)
+    assert f(W, O, -1, kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, O, 2, kmul // 2, None) == q.QGEMV_E_SHAPE
+    assert f(W, O, 0, kmul, None) == q.QGEMV_OK
+    assert f(None, O, 2, kmul, None) == q.QGEMV_E_NULL
+    assert f(W, None, 2, kmul, None) == q.QGEMV_E_NULL
+    assert f(W + 4, O, 2, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, O + 4, 2, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, W, 2, kmul, None) == q.QGEMV_E_ALIAS
+
+
+def test_read_ceiling_validation(q):
+    f = q.lib().qgemv_read_ceiling
+    assert f(A, 15, A + (1 << 32), None) == q.QGEMV_E_SHAPE
+    assert f(A, 0, A + (1 << 32), None) == q.QGEMV_OK
+    assert f(None, 1024, A + (1 << 32), None) == q.QGEMV_E_NULL
+    assert f(A + 4, 1024, A + (1 << 32), None) == q.QGEMV_E_ALIGN
+    assert f(A, 1024, A + 512, None) == q.QGEMV_E_ALIAS
+    assert q.qgemv_read_sink_len(1) == 1 and q.qgemv_read_sink_len(32768) == 1
+    assert q.qgemv_read_sink_len(32769) == 2
+
+
+def test_binding_rejects_host_tensors(q):
+    import torch
+
+    w = torch.zeros(144, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        q.qgemv_q4k(w, w, w, 1, 256)
