@@ -43,18 +43,19 @@ __global__ __launch_bounds__(512) void nvfp4_gemv_kernel(const uint8_t* __restri
   for (int ch = kwi; ch < kc; ch += kw) {
     const int e0 = ch * 2048 + 32 * lane;
     const bool valid = e0 < k;
+    // Activations first (loads complete in issue order), then all R rows.
+    unsigned X[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = ld128(xr, (uint32_t)e0 * 2u + 16u * i);
+      X[4 * i] = v.x; X[4 * i + 1] = v.y; X[4 * i + 2] = v.z; X[4 * i + 3] = v.w;
+    }
     u32x4 nib[R];
     unsigned sc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       nib[r] = ld128(nr, (uint32_t)(r * nib_row + ch * 1024 + 16 * lane));
       sc[r] = ld16(sr, (uint32_t)(r * sc_row + ch * 128 + 2 * lane));
-    }
-    unsigned X[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 v = ld128(xr, (uint32_t)e0 * 2u + 16u * i);
-      X[4 * i] = v.x; X[4 * i + 1] = v.y; X[4 * i + 2] = v.z; X[4 * i + 3] = v.w;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {

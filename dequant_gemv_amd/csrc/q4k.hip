@@ -84,7 +84,13 @@ __global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict
   for (int ch = kwi; ch < kc; ch += kw) {
     const int b = ch * 8 + bl;
     const bool valid = b < nb;
-    // Issue the weight loads of all R rows first: they are the long pole.
+    // The lane's 32 activations (16 of group 2c, 16 of group 2c+1) are loaded
+    // first: loads complete in issue order, so the rows below can be consumed
+    // one by one as they arrive instead of after the whole batch.
+    const uint32_t xo = (uint32_t)(b * 256 + 64 * c + 16 * h) * 2u;
+    const u32x4 xa0 = ld128(xr, xo), xa1 = ld128(xr, xo + 16);
+    const u32x4 xb0 = ld128(xr, xo + 64), xb1 = ld128(xr, xo + 80);
+    // Then the weights of all R rows, all in flight at once.
     u32x4 hdr[R], qs[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -92,10 +98,6 @@ __global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict
       hdr[r] = ld128(wr, off);
       qs[r] = ld128(wr, off + 16 + 16 * p);
     }
-    // The lane's 32 activations: 16 of group 2c and 16 of group 2c+1.
-    const uint32_t xo = (uint32_t)(b * 256 + 64 * c + 16 * h) * 2u;
-    const u32x4 xa0 = ld128(xr, xo), xa1 = ld128(xr, xo + 16);
-    const u32x4 xb0 = ld128(xr, xo + 64), xb1 = ld128(xr, xo + 80);
     const unsigned XA[8] = {xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
     const unsigned XB[8] = {xb0.x, xb0.y, xb0.z, xb0.w, xb1.x, xb1.y, xb1.z, xb1.w};
     // Pairs (x[4t], x[4t+2]) and (x[4t+1], x[4t+3]) match the two fp16 halves
@@ -138,8 +140,8 @@ __global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict
       const float d = f16lo(hdr[r].x), dmin = f16hi(hdr[r].x);
       const float v = __builtin_fmaf(sb, qb * 0.0625f, sa * qa);
       const float mx = __builtin_fmaf(mb, sxb, ma * sxa);
-      const float part = __builtin_fmaf(d, v, -dmin * mx);
-      acc[r] += valid ? part : 0.f;
+      const float t = __builtin_fmaf(-dmin, mx, __builtin_fmaf(d, v, acc[r]));
+      acc[r] = valid ? t : acc[r];
     }
   }
 

@@ -92,17 +92,12 @@ __global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict
   for (int ch = kwi; ch < kc; ch += kw) {
     const int nbs = min(kTq1SegBlocks, nb - ch * kTq1SegBlocks);  // blocks in this segment
     const bool active = lane < 54 && blk_first < nbs;
-    u32x4 raw[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      raw[r] = ld128(wr, (uint32_t)(r * row_bytes + ch * kTq1SegBytes + o0));
 
     // Per-lane activation pairs for 8 byte pairs x 5 digits, zero where the
-    // digit feeds no element of a block inside this segment.
+    // digit feeds no element of a block inside this segment.  Loaded before
+    // the weights: loads complete in issue order.
     unsigned xp[8][5];
-    float xs0 = 0.f, xs1 = 0.f;  // sum of x over the lane's elements, per slot
-    int bnd = 8;                 // byte pairs in the lane's first block
-    const unsigned kOnes = 0x3C003C00u;
+    int bnd = 8;  // byte pairs that belong to the lane's first block
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int o = o0 + 2 * i;
@@ -114,19 +109,36 @@ __global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict
       for (int k = 0; k < 5; ++k) {
         const int e = tq1_element(pos, k);
         const int ge = (ch * kTq1SegBlocks + blk) * 256 + e;
-        const unsigned v = ld32(xr, (uint32_t)ge * 2u);
-        xp[i][k] = (in && e >= 0) ? v : 0u;
-        if (blk == blk_first) xs0 = dot2h(xp[i][k], kOnes, xs0);
-        else xs1 = dot2h(xp[i][k], kOnes, xs1);
+        // an out-of-range offset reads as zero
+        xp[i][k] = ld32(xr, (in && e >= 0) ? (uint32_t)ge * 2u : 0xFFFFFFF0u);
       }
     }
-    // Which lane holds d of the blocks this lane touches, and where this
-    // lane's own d (if any) sits inside its 16 bytes.
-    int hold_off = -1;
+    // The d of a block sits in its bytes 52-53, inside exactly one lane's 16
+    // bytes; that lane loads it with a 16-bit load (a wider load could cross
+    // the end of the buffer and read as zero).
+    int hold = -1;
     for (int bh = blk_first; bh <= blk_first + 1; ++bh) {
       const int dpos = bh * kTq1Bytes + 52 - o0;
-      if (dpos >= 0 && dpos < 16) hold_off = dpos;
+      if (dpos >= 0 && dpos < 16 && bh < nbs && lane < 54) hold = bh * kTq1Bytes + 52;
     }
+    u32x4 raw[R];
+    unsigned short dbits[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t base = (uint32_t)(r * row_bytes + ch * kTq1SegBytes);
+      raw[r] = ld128(wr, base + o0);
+      dbits[r] = ld16(wr, hold >= 0 ? base + (uint32_t)hold : 0xFFFFFFF0u);
+    }
+
+    float xs0 = 0.f, xs1 = 0.f;  // sum of x over the lane's elements, per block slot
+    const unsigned kOnes = 0x3C003C00u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        if (i < bnd) xs0 = dot2h(xp[i][k], kOnes, xs0);
+        else xs1 = dot2h(xp[i][k], kOnes, xs1);
+      }
     const int src0 = ((blk_first * kTq1Bytes + 52) / 16) << 2;
     const int src1 = (((blk_first + 1) * kTq1Bytes + 52) / 16) << 2;
     const bool slot0 = active;
@@ -135,12 +147,7 @@ __global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const unsigned dw[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
-      // d held by this lane (0 if none)
-      unsigned hw = dw[0];
-      hw = (hold_off >> 2) == 1 ? dw[1] : hw;
-      hw = (hold_off >> 2) == 2 ? dw[2] : hw;
-      hw = (hold_off >> 2) == 3 ? dw[3] : hw;
-      const float dh = hold_off < 0 ? 0.f : ((hold_off & 2) ? f16hi(hw) : f16lo(hw));
+      const float dh = (float)__builtin_bit_cast(_Float16, dbits[r]);
       const float d0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src0, __builtin_bit_cast(int, dh)));
       const float d1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src1, __builtin_bit_cast(int, dh)));
 
@@ -154,9 +161,10 @@ __global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict
         for (int k = 0; k < 5; ++k) a = dot2h(D[k], xp[i][k], a);
         snap = (i == bnd - 1) ? a : snap;
       }
-      const float p0 = d0 * __builtin_fmaf(snap, 16384.f, -xs0);
-      const float p1 = d1 * __builtin_fmaf(a - snap, 16384.f, -xs1);
-      acc[r] += (slot0 ? p0 : 0.f) + (slot1 ? p1 : 0.f);
+      float t = acc[r];
+      t = slot0 ? __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0), t) : t;
+      t = slot1 ? __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1), t) : t;
+      acc[r] = t;
     }
   }
 
@@ -224,7 +232,7 @@ static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n
 
 hipError_t launch_tq1_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                            hipStream_t s) {
-  return launch_tq1_r<4>(w, x, y, n, k, s);
+  return launch_tq1_r<16>(w, x, y, n, k, s);
 }
 
 hipError_t launch_tq1_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
