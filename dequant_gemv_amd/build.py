@@ -22,8 +22,10 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build_id() -> str:
+def build_id(defines=()) -> str:
     h = hashlib.sha256()
+    for d in defines:
+        h.update(("-D" + d).encode())
     files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [os.path.join(INCLUDE, "qgemv.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -32,22 +34,24 @@ def build_id() -> str:
     return h.hexdigest()[:16]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out_path: str = LIB, defines=()) -> str:
+    """Compile every csrc/*.hip into one shared library.  `defines` (NAME=VALUE
+    strings) override the kernels' tuning constants; they enter the build id."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    out = LIB + ".tmp"
+    out = out_path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-fp32 VALU forms anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-result",
-           f"-DQGEMV_BUILD_ID=\"{build_id()}\"",
+           f"-DQGEMV_BUILD_ID=\"{build_id(defines)}\"", *("-D" + d for d in defines),
            "-I", INCLUDE, "-I", CSRC, *sources(), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stderr)
     if verbose:
         print(r.stderr)
-    os.replace(out, LIB)
-    return LIB
+    os.replace(out, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

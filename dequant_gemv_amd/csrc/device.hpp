@@ -18,12 +18,29 @@ constexpr int kWave = 64;
 // falls outside it return zero instead of touching memory, so ragged tails
 // (last rows, last K-chunk) need no address clamping.  Offsets are 32-bit, so
 // callers rebase `base` per workgroup and keep `bytes` below 2^31.
+// Callers pass wave-uniform values; readfirstlane makes that explicit so the
+// descriptor lives in SGPRs (a descriptor the compiler thinks divergent turns
+// every load into a per-lane waterfall loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Cache policy of the read-once weight stream (buffer-load aux bits; on
+// gfx950 bit 1 is the non-temporal hint).
+#ifndef QGEMV_WLOAD_AUX
+#define QGEMV_WLOAD_AUX 2  // nt: the weights are read once
+#endif
+__device__ __forceinline__ u32x4 ld128w(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, QGEMV_WLOAD_AUX);
 }
 __device__ __forceinline__ unsigned ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
@@ -59,6 +76,29 @@ __device__ __forceinline__ f32x2 fp4x2_f32(unsigned v, int sel) {
     case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
     case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
     default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+  }
+}
+
+// s_waitcnt vmcnt(n) for 0 <= n <= 15 (other counters untouched); the
+// switch folds once n is a constant.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
   }
 }
 

@@ -19,14 +19,22 @@
 
 namespace qgemv {
 
+// Rows per wave and waves per workgroup (tuning).
+#ifndef QGEMV_NVFP4_R
+#define QGEMV_NVFP4_R 8
+#endif
+#ifndef QGEMV_WG_WAVES
+#define QGEMV_WG_WAVES 8
+#endif
+
 template <int R>
-__global__ __launch_bounds__(512) void nvfp4_gemv_kernel(const uint8_t* __restrict__ w,
+__global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void nvfp4_gemv_kernel(const uint8_t* __restrict__ w,
                                                          const uint16_t* __restrict__ x,
                                                          float* __restrict__ y, int n, int k,
                                                          int kc, int kw, int rg) {
   __shared__ float red[16 * 16];
   const int lane = __lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer descriptors in SGPRs
   const int kwi = wave % kw;
   const int rgi = wave / kw;
   const int64_t nib_row = k / 2, sc_row = k / 16;
@@ -42,7 +50,11 @@ __global__ __launch_bounds__(512) void nvfp4_gemv_kernel(const uint8_t* __restri
 
   for (int ch = kwi; ch < kc; ch += kw) {
     const int e0 = ch * 2048 + 32 * lane;
+    // Lanes past K in a ragged chunk point at the end of the ranges: nibbles,
+    // scales and activations all read as zero and add exactly 0.
     const bool valid = e0 < k;
+    const uint32_t nib_off = valid ? (uint32_t)(ch * 1024 + 16 * lane) : (uint32_t)(nrows * nib_row);
+    const uint32_t sc_off = valid ? (uint32_t)(ch * 128 + 2 * lane) : (uint32_t)(nrows * sc_row);
     // Activations first (loads complete in issue order), then all R rows.
     unsigned X[16];
 #pragma unroll
@@ -54,8 +66,8 @@ __global__ __launch_bounds__(512) void nvfp4_gemv_kernel(const uint8_t* __restri
     unsigned sc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      nib[r] = ld128(nr, (uint32_t)(r * nib_row + ch * 1024 + 16 * lane));
-      sc[r] = ld16(sr, (uint32_t)(r * sc_row + ch * 128 + 2 * lane));
+      nib[r] = ld128w(nr, nib_off + (uint32_t)(r * nib_row));
+      sc[r] = ld16(sr, sc_off + (uint32_t)(r * sc_row));
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -70,8 +82,7 @@ __global__ __launch_bounds__(512) void nvfp4_gemv_kernel(const uint8_t* __restri
       }
       const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc[r], 0));
       const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc[r], 1));
-      const float part = __builtin_fmaf(s1, a1, s0 * a0);
-      acc[r] += valid ? part : 0.f;
+      acc[r] = __builtin_fmaf(s1, a1, __builtin_fmaf(s0, a0, acc[r]));
     }
   }
 
@@ -123,8 +134,8 @@ template <int R>
 static hipError_t launch_nvfp4_r(const void* w, const void* x, float* y, int64_t n, int64_t k,
                                  hipStream_t s) {
   const int kc = (int)((k + 2047) / 2048);
-  const int kw = kc < 8 ? kc : 8;
-  const int rg = kw >= 8 ? 1 : 8 / kw;
+  const int kw = kc < QGEMV_WG_WAVES ? kc : QGEMV_WG_WAVES;
+  const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
   const int rows_per_wg = rg * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL(nvfp4_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
@@ -134,7 +145,7 @@ static hipError_t launch_nvfp4_r(const void* w, const void* x, float* y, int64_t
 
 hipError_t launch_nvfp4_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                              hipStream_t s) {
-  return launch_nvfp4_r<8>(w, x, y, n, k, s);
+  return launch_nvfp4_r<QGEMV_NVFP4_R>(w, x, y, n, k, s);
 }
 
 hipError_t launch_nvfp4_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {

@@ -30,6 +30,14 @@
 
 namespace qgemv {
 
+// Rows per wave and waves per workgroup (tuning).
+#ifndef QGEMV_Q4K_R
+#define QGEMV_Q4K_R 8
+#endif
+#ifndef QGEMV_WG_WAVES
+#define QGEMV_WG_WAVES 8
+#endif
+
 constexpr int kQ4kBytes = 144;
 
 // 6-bit scale and min of the two consecutive groups (2c, 2c+1) a lane owns,
@@ -58,13 +66,13 @@ struct Q4kScaleSel {
 };
 
 template <int R>
-__global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict__ w,
+__global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void q4k_gemv_kernel(const uint8_t* __restrict__ w,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int n, int nb,
                                                        int kc, int kw, int rg) {
   __shared__ float red[16 * 16];
   const int lane = __lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer descriptors in SGPRs
   const int kwi = wave % kw;
   const int rgi = wave / kw;
   const int64_t row_bytes = (int64_t)nb * kQ4kBytes;
@@ -83,7 +91,10 @@ __global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict
 
   for (int ch = kwi; ch < kc; ch += kw) {
     const int b = ch * 8 + bl;
-    const bool valid = b < nb;
+    // Lanes past the last block of a ragged chunk point at the end of the
+    // range: their loads read zeros (d = dmin = q = 0) and add exactly 0, so
+    // no lane needs a branch or a select around the loaded data.
+    const uint32_t lane_off = b < nb ? (uint32_t)(b * kQ4kBytes) : (uint32_t)(nrows * row_bytes);
     // The lane's 32 activations (16 of group 2c, 16 of group 2c+1) are loaded
     // first: loads complete in issue order, so the rows below can be consumed
     // one by one as they arrive instead of after the whole batch.
@@ -94,9 +105,9 @@ __global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict
     u32x4 hdr[R], qs[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint32_t off = (uint32_t)(r * row_bytes + b * kQ4kBytes);
-      hdr[r] = ld128(wr, off);
-      qs[r] = ld128(wr, off + 16 + 16 * p);
+      const uint32_t off = lane_off + (uint32_t)(r * row_bytes);
+      hdr[r] = ld128w(wr, off);
+      qs[r] = ld128w(wr, off + 16 + 16 * p);
     }
     const unsigned XA[8] = {xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
     const unsigned XB[8] = {xb0.x, xb0.y, xb0.z, xb0.w, xb1.x, xb1.y, xb1.z, xb1.w};
@@ -140,8 +151,7 @@ __global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict
       const float d = f16lo(hdr[r].x), dmin = f16hi(hdr[r].x);
       const float v = __builtin_fmaf(sb, qb * 0.0625f, sa * qa);
       const float mx = __builtin_fmaf(mb, sxb, ma * sxa);
-      const float t = __builtin_fmaf(-dmin, mx, __builtin_fmaf(d, v, acc[r]));
-      acc[r] = valid ? t : acc[r];
+      acc[r] = __builtin_fmaf(-dmin, mx, __builtin_fmaf(d, v, acc[r]));
     }
   }
 
@@ -150,6 +160,131 @@ __global__ __launch_bounds__(512) void q4k_gemv_kernel(const uint8_t* __restrict
   constexpr int kLanesPerRow = 64 >> L;
   if ((lane & (kLanesPerRow - 1)) == 0)
     red[(rgi * kw + kwi) * R + (lane >> (6 - L))] = acc[0];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < rg * R) {
+    const int g = t / R, r = t % R;
+    float s = 0.f;
+    for (int k = 0; k < kw; ++k) s += red[(g * kw + k) * R + r];
+    const int row = blockIdx.x * rg * R + g * R + r;
+    if (row < n) y[row] = s * 0x1p24f;
+  }
+}
+
+// LDS-transposed variant of the GEMV above.  A wave owns one K-chunk of 8
+// blocks for a batch of 8 rows: 8 x 1152 contiguous-per-row bytes = 9 KiB,
+// read with nine dwordx4 loads of one 16-byte piece per lane.  Every load is
+// one 1 KiB run starting on a 128-byte line (1152 = 9*128 and a row of a
+// multiple of 8 blocks is a multiple of 1152 bytes).  Each piece is written to
+// the wave's slice of LDS as it arrives and lanes read their 16-byte nibble
+// slice and the block header back with ds_read_b128 (the header read is a
+// broadcast among 8 lanes), a row at a time as soon as its pieces are in.
+// Chunks beyond the wave's first are processed in turn through the same LDS.
+constexpr int kQ4kBatchRows = 8;
+constexpr int kQ4kStage = kQ4kBatchRows * 8 * kQ4kBytes;  // 9216 bytes per wave
+
+__global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void q4k_gemv_lds_kernel(const uint8_t* __restrict__ w,
+                                                                          const uint16_t* __restrict__ x,
+                                                                          float* __restrict__ y, int n, int nb,
+                                                                          int kc, int kw, int rg) {
+  __shared__ __attribute__((aligned(16))) unsigned char stage_all[QGEMV_WG_WAVES * kQ4kStage];
+  __shared__ float red[QGEMV_WG_WAVES * kQ4kBatchRows];
+  constexpr int R = kQ4kBatchRows;
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kwi = wave % kw;
+  const int rgi = wave / kw;
+  const int64_t row_bytes = (int64_t)nb * kQ4kBytes;
+  const int row0 = blockIdx.x * rg * R + rgi * R;
+  const int nrows = max(0, min(R, n - row0));
+  const uint32_t range = (uint32_t)(nrows * row_bytes);
+  const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, range);
+  const auto xr = make_rsrc(x, (uint32_t)nb * 512u);
+  unsigned char* stage = stage_all + wave * kQ4kStage;
+
+  const int bl = lane >> 3, p = lane & 7, c = p >> 1, h = p & 1;
+  const Q4kScaleSel sel(c);
+  const unsigned kOnes = 0x3C003C00u;
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+  for (int ch = kwi; ch < kc; ch += kw) {
+    const int b = ch * 8 + bl;
+    const int nbc = min(8, nb - ch * 8);  // blocks of this chunk inside the row
+    // activations first: loads complete in issue order
+    const uint32_t xo = (uint32_t)(b * 256 + 64 * c + 16 * h) * 2u;
+    const u32x4 xa0 = ld128(xr, xo), xa1 = ld128(xr, xo + 16);
+    const u32x4 xb0 = ld128(xr, xo + 64), xb1 = ld128(xr, xo + 80);
+    // The batch: nine coalesced 1 KiB loads (one 16-byte piece per lane),
+    // all in flight at once.
+    u32x4 pc[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int piece = 64 * i + lane;         // 16-byte piece of the 8 x 1152-byte batch
+      const int rr = piece / 72, within = piece % 72;
+      const bool inside = within < nbc * 9;    // past the row's last block: read zeros
+      const uint32_t off = inside ? (uint32_t)(rr * row_bytes + ch * 8 * kQ4kBytes + within * 16) : range;
+      pc[i] = ld128w(wr, off);
+    }
+    const unsigned XA[8] = {xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
+    const unsigned XB[8] = {xb0.x, xb0.y, xb0.z, xb0.w, xb1.x, xb1.y, xb1.z, xb1.w};
+    unsigned pa02[4], pa13[4], pb02[4], pb13[4];
+    float sxa = 0.f, sxb = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pa02[t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x05040100u);
+      pa13[t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x07060302u);
+      pb02[t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x05040100u);
+      pb13[t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x07060302u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sxa = dot2h(XA[i], kOnes, sxa);
+      sxb = dot2h(XB[i], kOnes, sxb);
+    }
+    sxa *= 0x1p-24f;
+    sxb *= 0x1p-24f;
+    // the previous chunk's LDS reads are done before its slice is rewritten
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    int written = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // Row r lies in pieces 72r .. 72r+71, i.e. in loads 0 .. (72r+71)/64.
+      // Each load is written to LDS right after it lands (loads complete in
+      // issue order), so row r is consumed as soon as its two loads are in.
+      const int need = (72 * r + 71) / 64;
+#pragma unroll
+      for (int i = 0; i < 9; ++i)
+        if (i >= written && i <= need) *reinterpret_cast<u32x4*>(stage + 1024 * i + 16 * lane) = pc[i];
+      written = need + 1;
+      const unsigned char* blk = stage + r * 8 * kQ4kBytes + bl * kQ4kBytes;
+      const u32x4 hdr = *reinterpret_cast<const u32x4*>(blk);
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * p);
+      const unsigned q[4] = {qv.x, qv.y, qv.z, qv.w};
+      float qa = 0.f, qb = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const unsigned w0 = q[t], w8 = q[t] >> 8;
+        qa = dot2h(w0 & 0x000F000Fu, pa02[t], qa);
+        qa = dot2h(w8 & 0x000F000Fu, pa13[t], qa);
+        qb = dot2h(w0 & 0x00F000F0u, pb02[t], qb);
+        qb = dot2h(w8 & 0x00F000F0u, pb13[t], qb);
+      }
+      const unsigned sp = sel.scales(hdr.y, hdr.w);
+      const unsigned mp = sel.mins(hdr.z, hdr.w);
+      const float sa = (float)(sp & 0xFFu), sb = (float)((sp >> 8) & 0xFFu);
+      const float ma = (float)(mp & 0xFFu), mb = (float)((mp >> 8) & 0xFFu);
+      const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
+      const float v = __builtin_fmaf(sb, qb * 0.0625f, sa * qa);
+      const float mx = __builtin_fmaf(mb, sxb, ma * sxa);
+      acc[r] = __builtin_fmaf(-dmin, mx, __builtin_fmaf(d, v, acc[r]));
+    }
+  }
+
+  wave_reduce_rows<R>(acc);
+  if ((lane & 7) == 0) red[(rgi * kw + kwi) * R + (lane >> 3)] = acc[0];
   __syncthreads();
   const int t = threadIdx.x;
   if (t < rg * R) {
@@ -199,8 +334,8 @@ static hipError_t launch_q4k_r(const void* w, const void* x, float* y, int64_t n
                                hipStream_t s) {
   const int nb = (int)(k / 256);
   const int kc = (nb + 7) / 8;
-  const int kw = kc < 8 ? kc : 8;
-  const int rg = kw >= 8 ? 1 : 8 / kw;
+  const int kw = kc < QGEMV_WG_WAVES ? kc : QGEMV_WG_WAVES;
+  const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
   const int rows_per_wg = rg * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL(q4k_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
@@ -208,9 +343,28 @@ static hipError_t launch_q4k_r(const void* w, const void* x, float* y, int64_t n
   return hipGetLastError();
 }
 
+static hipError_t launch_q4k_lds(const void* w, const void* x, float* y, int64_t n, int64_t k,
+                                 hipStream_t s) {
+  const int nb = (int)(k / 256);
+  const int kc = (nb + 7) / 8;
+  const int kw = kc < QGEMV_WG_WAVES ? kc : QGEMV_WG_WAVES;
+  const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
+  const int rows_per_wg = rg * kQ4kBatchRows;
+  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(q4k_gemv_lds_kernel, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, nb, kc, kw, rg);
+  return hipGetLastError();
+}
+
+// 0: register-staged kernel, 1: LDS-staged kernel
+#ifndef QGEMV_Q4K_IMPL
+#define QGEMV_Q4K_IMPL 1
+#endif
+
 hipError_t launch_q4k_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                            hipStream_t s) {
-  return launch_q4k_r<8>(w, x, y, n, k, s);
+  if (QGEMV_Q4K_IMPL == 1) return launch_q4k_lds(w, x, y, n, k, s);
+  return launch_q4k_r<QGEMV_Q4K_R>(w, x, y, n, k, s);
 }
 
 hipError_t launch_q4k_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {

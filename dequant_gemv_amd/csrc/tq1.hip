@@ -34,6 +34,14 @@
 
 namespace qgemv {
 
+// Rows per wave and waves per workgroup (tuning).
+#ifndef QGEMV_TQ1_R
+#define QGEMV_TQ1_R 8
+#endif
+#ifndef QGEMV_WG_WAVES
+#define QGEMV_WG_WAVES 8
+#endif
+
 constexpr int kTq1Bytes = 54;
 constexpr int kTq1SegBlocks = 16;
 constexpr int kTq1SegBytes = kTq1SegBlocks * kTq1Bytes;  // 864 = 54 * 16
@@ -67,13 +75,13 @@ __device__ __forceinline__ void tq1_digits(unsigned B, unsigned (&D)[5]) {
 }
 
 template <int R>
-__global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict__ w,
+__global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void tq1_gemv_kernel(const uint8_t* __restrict__ w,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int n, int nb,
                                                        int kc, int kw, int rg) {
   __shared__ float red[16 * 16];
   const int lane = __lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer descriptors in SGPRs
   const int kwi = wave % kw;
   const int rgi = wave / kw;
   const int64_t row_bytes = (int64_t)nb * kTq1Bytes;
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t base = (uint32_t)(r * row_bytes + ch * kTq1SegBytes);
-      raw[r] = ld128(wr, base + o0);
+      raw[r] = ld128w(wr, base + o0);
       dbits[r] = ld16(wr, hold >= 0 ? base + (uint32_t)hold : 0xFFFFFFF0u);
     }
 
@@ -136,13 +144,14 @@ __global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int k = 0; k < 5; ++k) {
-        if (i < bnd) xs0 = dot2h(xp[i][k], kOnes, xs0);
-        else xs1 = dot2h(xp[i][k], kOnes, xs1);
+        xs0 = dot2h(i < bnd ? xp[i][k] : 0u, kOnes, xs0);
+        xs1 = dot2h(i < bnd ? 0u : xp[i][k], kOnes, xs1);
       }
+    // A slot whose block lies outside the segment (or a lane past the
+    // payload) gets d = 0 from a non-holding lane and zero coefficients, so
+    // it adds exactly 0 without a branch.
     const int src0 = ((blk_first * kTq1Bytes + 52) / 16) << 2;
     const int src1 = (((blk_first + 1) * kTq1Bytes + 52) / 16) << 2;
-    const bool slot0 = active;
-    const bool slot1 = active && bnd < 8 && blk_first + 1 < nbs;
 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -161,10 +170,8 @@ __global__ __launch_bounds__(512) void tq1_gemv_kernel(const uint8_t* __restrict
         for (int k = 0; k < 5; ++k) a = dot2h(D[k], xp[i][k], a);
         snap = (i == bnd - 1) ? a : snap;
       }
-      float t = acc[r];
-      t = slot0 ? __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0), t) : t;
-      t = slot1 ? __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1), t) : t;
-      acc[r] = t;
+      float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0), acc[r]);
+      acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1), t);
     }
   }
 
@@ -221,8 +228,8 @@ static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n
                                hipStream_t s) {
   const int nb = (int)(k / 256);
   const int kc = (nb + kTq1SegBlocks - 1) / kTq1SegBlocks;
-  const int kw = kc < 8 ? kc : 8;
-  const int rg = kw >= 8 ? 1 : 8 / kw;
+  const int kw = kc < QGEMV_WG_WAVES ? kc : QGEMV_WG_WAVES;
+  const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
   const int rows_per_wg = rg * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL(tq1_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
@@ -232,7 +239,7 @@ static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n
 
 hipError_t launch_tq1_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                            hipStream_t s) {
-  return launch_tq1_r<16>(w, x, y, n, k, s);
+  return launch_tq1_r<QGEMV_TQ1_R>(w, x, y, n, k, s);
 }
 
 hipError_t launch_tq1_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
