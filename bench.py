@@ -44,6 +44,25 @@ def algorithmic_bytes(fmt: str, n: int, k: int) -> int:
     return synth.weight_bytes(fmt, n, k) + 2 * k + 4 * n
 
 
+TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "q4k_gemv_4096x14336_hbm_bytes.md")
+
+
+def measured_traffic(build_id: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE
+    summary, only if it was taken with this very build of the library."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_SUMMARY) if ":" in line)
+    except OSError:
+        return None
+    if fields.get("traffic_build_id", "").strip() != build_id:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -185,6 +204,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--fmt", default=None, help="measure only this format (q4k, nvfp4, tq1) at N,K")
     ap.add_argument("--n", type=int, default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 64 MiB device copy (a known-size reference for the HBM byte counters)")
     ap.add_argument("--k", type=int, default=None)
     args = ap.parse_args()
 
@@ -202,6 +223,15 @@ def main():
     if want != have:
         print(f"libqgemv.so build id {have} does not match the sources ({want}); rebuild", file=sys.stderr)
         sys.exit(3)
+
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration: 8 copies of 64 MiB (read 65536 KiB + write 65536 KiB each)")
 
     fmt, n, k, desc = MAIN
     if args.fmt:
@@ -257,7 +287,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(have) if (fmt, n, k) == MAIN[:3] else None,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "us_per_gemv": round(main_res["us_per_launch_event"], 3),
