@@ -137,6 +137,79 @@ __device__ __forceinline__ void wave_reduce_rows(float (&v)[R]) {
   }
 }
 
+
+// s_waitcnt vmcnt(N) for a compile-time 0 <= N <= 63 (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima, i.e. no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One wave-wide 16-byte-per-lane buffer load straight into LDS: lane i's
+// bytes [voff, voff+16) of the descriptor land at lds + 16*i (the LDS base is
+// wave-uniform).  Bytes outside the descriptor's range land as zeros.
+// Completion is counted by vmcnt like any other buffer load.
+template <int AUX = 0>
+__device__ __forceinline__ void ld128_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, AUX);
+}
+
+// Compile-time loop: calls f(Int<I>{}) for I = B .. E-1, so the body can use
+// its index in constant expressions (wait counts, register array indices).
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Int<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_ror4(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {  // quad_perm [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float dpp_bcast15(float v) {  // rows 1, 3 read lane 15 of the row before
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+}
+__device__ __forceinline__ float dpp_bcast31(float v) {  // rows 2, 3 read lane 31
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+}
+
+// Sum each of R per-lane values over the 64 lanes of the wave with DPP only
+// (no LDS round trip): rotations and quad permutes sum each 16-lane row into
+// all of its lanes, then two row broadcasts carry rows 0-2 into row 3.  On
+// return lanes 48-63 hold every total; the other lanes hold partial sums.
+template <int R>
+__device__ __forceinline__ void wave_reduce_dpp(float (&v)[R]) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float t = v[i];
+    t += dpp_ror8(t);
+    t += dpp_ror4(t);
+    t += dpp_xor2(t);
+    t += dpp_xor1(t);
+    t += dpp_bcast15(t);
+    t += dpp_bcast31(t);
+    v[i] = t;
+  }
+}
+
 template <int R>
 __device__ __forceinline__ constexpr int log2i() {
   return R <= 1 ? 0 : 1 + log2i<R / 2>();

@@ -296,6 +296,188 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void q4k_gemv_lds_kernel(const
   }
 }
 
+
+// Row-streaming variant: W waves per workgroup (one or two per SIMD), each
+// wave owning R whole rows (all K) so no partial sum ever leaves the wave.
+// Everything a wave reads is one contiguous run of R row records (at most
+// 36 KiB), streamed with coalesced 1 KiB buffer loads that land straight in
+// the wave's LDS stage (no VGPRs, no LDS writes).  A wave keeps only a few
+// loads in flight ahead of the unit it is consuming and issues the next one
+// as each unit is done: a CU's memory pipeline holds a bounded number of
+// requests and a wave that tries to issue past that stalls at the load, so
+// issuing everything up front would hold back the arithmetic (and the
+// workgroup barrier below) until most of the data had already arrived.  The activations are
+// read once per workgroup the same way into LDS, swizzled in 16-byte granules
+// so that the per-lane reads below hit 8 distinct bank groups, and then held
+// in registers for every K-chunk.
+//
+// Unit (r, ch) = the 8 blocks of chunk ch of row r (1152 bytes).  Lane l takes
+// block l/8 and nibble slice l%8 of each unit exactly as the K-split kernel
+// does, and consumes the unit as soon as the loads covering it are in (loads
+// complete in issue order, so one vmcnt wait per unit).  The R row partials
+// are summed across the wave with DPP (no LDS), and lanes 48..48+R-1 store
+// one row each.
+// Granule (16 bytes = 8 activations) swizzle of the activation copy in LDS.
+// Granule g of a 512-byte block holds elements 8g..8g+7; a lane with chunk
+// position c = (g >> 3) & 3 reads granules 8c + {0,1,4,5} + 2h, so XOR-ing bits
+// 0 and 2 of g with c's two bits spreads the 8 lanes of a block over 8
+// different 16-byte bank groups.  The map is its own inverse.
+__device__ __forceinline__ constexpr int q4k_xswz(int g) {
+  return g ^ (((g >> 3) & 1) | (((g >> 4) & 1) << 2));
+}
+
+#ifndef QGEMV_Q4K_AHEAD
+#define QGEMV_Q4K_AHEAD 6  // weight loads in flight per wave beyond the unit being consumed
+#endif
+
+template <int KC, int R, int W>
+struct Q4kRows {
+  static constexpr int kUnitBytes = 8 * kQ4kBytes;                        // 1152
+  static constexpr int kLoads = (R * KC * kUnitBytes + 1023) / 1024;      // weight loads per wave
+  static constexpr int kStage = kLoads * 1024;                            // LDS bytes per wave
+  static constexpr int kXBytes = KC * 4096;                               // activations in LDS
+  static constexpr int kLds = W * kStage + kXBytes;
+  static constexpr int kXLoads = (4 * KC + W - 1) / W;                    // activation loads per wave (at most)
+  static_assert(KC >= 1 && KC <= 8, "K-chunk count");
+  static_assert(KC + kLoads < 64, "vmcnt holds at most 63 outstanding loads");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  // Last load unit u (= r*KC + ch) can depend on, for the largest row record
+  // (8*KC blocks; shorter records only end earlier).
+  static constexpr int last_load(int u) { return (u * kUnitBytes + kUnitBytes - 1) / 1024; }
+  // Weight loads issued before unit u is consumed: the first kAhead up front,
+  // then after each unit enough to stay kAhead loads past it.
+  static constexpr int kAhead = QGEMV_Q4K_AHEAD;
+  static_assert(kAhead >= 2, "a unit spans up to two loads");
+  static constexpr int issued_before(int u) {
+    int n = kAhead < kLoads ? kAhead : kLoads;
+    for (int v = 0; v < u; ++v) {
+      const int t = last_load(v) + 1 + kAhead;
+      n = t > n ? (t < kLoads ? t : kLoads) : n;
+    }
+    return n;
+  }
+};
+
+template <int KC, int R, int W>
+__global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __restrict__ w,
+                                                                      const uint16_t* __restrict__ x,
+                                                                      float* __restrict__ y, int n, int nb) {
+  using C = Q4kRows<KC, R, W>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
+  unsigned char* const xs = lds + W * C::kStage;
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned char* const stage = lds + wave * C::kStage;
+  const int row_bytes = nb * kQ4kBytes;
+  const int row0 = (blockIdx.x * W + wave) * R;
+  const int nrows = max(0, min(R, n - row0));
+
+  // Activations first: the workgroup's 4*KC one-KiB pieces, dealt to the
+  // waves in turn.
+  {
+    const auto xr = make_rsrc(x, (uint32_t)nb * 512u);
+    const int g = lane & 31;
+    const uint32_t src = (uint32_t)((lane & 32) + q4k_xswz(g)) * 16u;
+#pragma unroll
+    for (int i = 0; i < C::kXLoads; ++i) {
+      const int piece = i * W + wave;
+      if (piece < 4 * KC) ld128_lds(xr, xs + piece * 1024, (uint32_t)piece * 1024u + src);
+    }
+  }
+  // Then the first weight loads of the wave's rows.
+  const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, (uint32_t)(nrows * row_bytes));
+  static_for<0, C::issued_before(0)>([&](auto i) {
+    ld128_lds<QGEMV_WLOAD_AUX>(wr, stage + decltype(i)::value * 1024, (uint32_t)(decltype(i)::value * 1024 + 16 * lane));
+  });
+
+  const int bl = lane >> 3, p = lane & 7, c = p >> 1, h = p & 1;
+  const Q4kScaleSel sel(c);
+  const unsigned kOnes = 0x3C003C00u;
+
+  wait_vm<C::issued_before(0)>();  // this wave's activation pieces (issued before the weights) are in LDS
+  __builtin_amdgcn_s_barrier();  // ... and every other wave's
+
+  // The lane's activations for every chunk, as fp16 pairs matching the masked
+  // nibble layout, and their group sums (times 2^-24, see the K-split kernel).
+  unsigned pa02[KC][4], pa13[KC][4], pb02[KC][4], pb13[KC][4];
+  float sxa[KC], sxb[KC];
+#pragma unroll
+  for (int ch = 0; ch < KC; ++ch) {
+    const unsigned char* xb = xs + (ch * 8 + bl) * 512;
+    const int g0 = 8 * c + 2 * h;
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(xb + 16 * q4k_xswz(g0));
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(xb + 16 * q4k_xswz(g0 + 1));
+    const u32x4 b0 = *reinterpret_cast<const u32x4*>(xb + 16 * q4k_xswz(g0 + 4));
+    const u32x4 b1 = *reinterpret_cast<const u32x4*>(xb + 16 * q4k_xswz(g0 + 5));
+    const unsigned XA[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const unsigned XB[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pa02[ch][t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x05040100u);
+      pa13[ch][t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x07060302u);
+      pb02[ch][t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x05040100u);
+      pb13[ch][t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x07060302u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sa = dot2h(XA[i], kOnes, sa);
+      sb = dot2h(XB[i], kOnes, sb);
+    }
+    sxa[ch] = sa * 0x1p-24f;
+    sxb[ch] = sb * 0x1p-24f;
+  }
+
+  // Lanes past the row's last block in a ragged last chunk see the next
+  // record's bytes (or zeros); their share is dropped.
+  const bool tail_ok = (KC - 1) * 8 + bl < nb;
+
+  static_assert(R <= 16, "one row per lane of the last 16-lane row");
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  static_for<0, R * KC>([&](auto u) {
+    constexpr int U = decltype(u)::value, r = U / KC, ch = U % KC;
+    wait_vm<C::issued_before(U) - 1 - C::last_load(U)>();
+    const unsigned char* blk = stage + r * row_bytes + ch * C::kUnitBytes + bl * kQ4kBytes;
+    const u32x4 hdr = *reinterpret_cast<const u32x4*>(blk);
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * p);
+    const unsigned q[4] = {qv.x, qv.y, qv.z, qv.w};
+    float qa = 0.f, qb = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const unsigned w0 = q[t], w8 = q[t] >> 8;
+      qa = dot2h(w0 & 0x000F000Fu, pa02[ch][t], qa);
+      qa = dot2h(w8 & 0x000F000Fu, pa13[ch][t], qa);
+      qb = dot2h(w0 & 0x00F000F0u, pb02[ch][t], qb);
+      qb = dot2h(w8 & 0x00F000F0u, pb13[ch][t], qb);
+    }
+    const unsigned sp = sel.scales(hdr.y, hdr.w);
+    const unsigned mp = sel.mins(hdr.z, hdr.w);
+    const float sa = (float)(sp & 0xFFu), sb = (float)((sp >> 8) & 0xFFu);
+    const float ma = (float)(mp & 0xFFu), mb = (float)((mp >> 8) & 0xFFu);
+    const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
+    const float v = __builtin_fmaf(sb, qb * 0.0625f, sa * qa);
+    const float mx = __builtin_fmaf(mb, sxb[ch], ma * sxa[ch]);
+    const float part = __builtin_fmaf(-dmin, mx, d * v);
+    if constexpr (ch == KC - 1)
+      acc[r] += tail_ok ? part : 0.f;
+    else
+      acc[r] += part;
+    // refill: this unit's LDS reads have completed (their data was used above)
+    static_for<C::issued_before(U), C::issued_before(U + 1)>([&](auto i) {
+      ld128_lds<QGEMV_WLOAD_AUX>(wr, stage + decltype(i)::value * 1024, (uint32_t)(decltype(i)::value * 1024 + 16 * lane));
+    });
+  });
+
+  wave_reduce_dpp<R>(acc);
+  const int j = lane & 15;
+  float t = acc[0];
+#pragma unroll
+  for (int s = 1; s < R; ++s) t = j == s ? acc[s] : t;
+  if (lane >= 48 && j < nrows) y[row0 + j] = t * 0x1p24f;
+}
+
 // One thread per (block, 16-byte nibble slice): 32 weights, written as the
 // correctly rounded fp32 of d*s*q - dmin*m (both products are exact in fp32,
 // so one fma rounds once).
@@ -356,14 +538,62 @@ static hipError_t launch_q4k_lds(const void* w, const void* x, float* y, int64_t
   return hipGetLastError();
 }
 
-// 0: register-staged kernel, 1: LDS-staged kernel
+
+// Row-streaming launch for the K-chunk counts it is instantiated for: R rows
+// per wave chosen so the grid is about one wave per SIMD (one-shot), capped by
+// the LDS stage; returns false when the shape has no instantiation.
+template <int KC, int R, int W>
+static hipError_t launch_q4k_rows_r(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+  const int64_t rows_per_wg = (int64_t)W * R;
+  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((q4k_gemv_rows_kernel<KC, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)(k / 256));
+  return hipGetLastError();
+}
+
+// Shape -> (R rows per wave, W waves per workgroup).  Up to 1024 rows: one
+// row per wave, 4 waves per workgroup (up to one wave per SIMD).  Beyond: 8
+// waves (two per SIMD, so one wave's LDS latency hides behind the other's
+// arithmetic) and R = ceil(N / 2048), i.e. about 256 workgroups that all run
+// at once; for N past what fits, a smaller stage so two workgroups share a CU
+// and one's loads overlap the other's tail.
+static bool launch_q4k_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s,
+                            hipError_t* err) {
+  const int nb = (int)(k / 256);
+  const int kc = (nb + 7) / 8;
+  const int64_t r8 = (n + 2047) / 2048;
+  if (kc == 7) {
+    if (n <= 1024) *err = launch_q4k_rows_r<7, 1, 4>(w, x, y, n, k, s);
+    else if (r8 <= 1) *err = launch_q4k_rows_r<7, 1, 8>(w, x, y, n, k, s);
+    else *err = launch_q4k_rows_r<7, 2, 8>(w, x, y, n, k, s);
+    return true;
+  }
+  if (kc == 2) {
+    if (n <= 1024) *err = launch_q4k_rows_r<2, 1, 4>(w, x, y, n, k, s);
+    else if (r8 <= 1) *err = launch_q4k_rows_r<2, 1, 8>(w, x, y, n, k, s);
+    else if (r8 <= 2) *err = launch_q4k_rows_r<2, 2, 8>(w, x, y, n, k, s);
+    else if (r8 <= 4) *err = launch_q4k_rows_r<2, 4, 8>(w, x, y, n, k, s);
+    else if (r8 <= 7) *err = launch_q4k_rows_r<2, 7, 8>(w, x, y, n, k, s);
+    else if (r8 <= 8) *err = launch_q4k_rows_r<2, 8, 8>(w, x, y, n, k, s);
+    else *err = launch_q4k_rows_r<2, 4, 8>(w, x, y, n, k, s);
+    return true;
+  }
+  return false;
+}
+
+// 0: register-staged kernel, 1: LDS-staged K-split kernel, 2: row-streaming
+// kernel where instantiated (K-split otherwise)
 #ifndef QGEMV_Q4K_IMPL
-#define QGEMV_Q4K_IMPL 1
+#define QGEMV_Q4K_IMPL 2
 #endif
 
 hipError_t launch_q4k_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                            hipStream_t s) {
-  if (QGEMV_Q4K_IMPL == 1) return launch_q4k_lds(w, x, y, n, k, s);
+  if (QGEMV_Q4K_IMPL == 2) {
+    hipError_t e = hipSuccess;
+    if (launch_q4k_rows(w, x, y, n, k, s, &e)) return e;
+  }
+  if (QGEMV_Q4K_IMPL >= 1) return launch_q4k_lds(w, x, y, n, k, s);
   return launch_q4k_r<QGEMV_Q4K_R>(w, x, y, n, k, s);
 }
 

@@ -128,6 +128,8 @@ SMALL = [
     # (fmt, n, k): several K-chunks, row groups and ragged tails
     ("q4k", 1, 256), ("q4k", 5, 512), ("q4k", 37, 2304), ("q4k", 129, 4096), ("q4k", 77, 14336),
     ("q4k", 300, 18432), ("q4k", 65, 36864),
+    # row-streaming Q4_K: ragged last K-chunk at 7 chunks, 2 / 4 / 8 rows per wave
+    ("q4k", 300, 13056), ("q4k", 1500, 14336), ("q4k", 1500, 2304), ("q4k", 3000, 3328), ("q4k", 5000, 4096), ("q4k", 16000, 2560),
     ("nvfp4", 1, 32), ("nvfp4", 3, 96), ("nvfp4", 37, 2080), ("nvfp4", 129, 4096), ("nvfp4", 77, 14336),
     ("nvfp4", 65, 36896),
     ("tq1", 1, 256), ("tq1", 5, 768), ("tq1", 37, 4352), ("tq1", 129, 4096), ("tq1", 77, 14336),
