@@ -16,6 +16,7 @@
 // (algebraically equal to scaling each weight; only the rounding order moves).
 #include "device.hpp"
 #include "launch.hpp"
+#include "stream.hpp"
 
 namespace qgemv {
 
@@ -102,6 +103,91 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void nvfp4_gemv_kernel(const u
   }
 }
 
+
+// Row-streaming variant (K a multiple of 2048): a wave owns R whole rows.
+// Its nibbles are one contiguous run of R*K/2 bytes in which unit u = r*KC +
+// ch (row r, K-chunk ch of 2048 weights) is exactly load u; its scales are a
+// second run of R*K/16 bytes, loaded up front.  Both land in the wave's LDS
+// stage.  The activations are copied once per workgroup into LDS with each
+// 64-byte lane slice spread as four 16-byte granules 1 KiB apart (so each of
+// a lane's four reads is one contiguous 1 KiB across the wave) and held in
+// registers for every chunk.  Lane l takes weights 32l..32l+31 of each chunk
+// as in the K-split kernel; row totals are summed with DPP.
+#ifndef QGEMV_NVFP4_AHEAD
+#define QGEMV_NVFP4_AHEAD 4
+#endif
+
+template <int KC, int R, int W>
+struct Nvfp4Rows {
+  using S = StreamSchedule<1024, R * KC, QGEMV_NVFP4_AHEAD, QGEMV_NVFP4_AHEAD>;
+  static constexpr int kScLoads = (R * KC * 128 + 1023) / 1024;
+  static constexpr int kStage = kScLoads * 1024 + S::kStage;
+  static constexpr int kLds = W * kStage + KC * 4096;
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+};
+
+template <int KC, int R, int W>
+__global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* __restrict__ w,
+                                                                const uint16_t* __restrict__ x,
+                                                                float* __restrict__ y, int n) {
+  using C = Nvfp4Rows<KC, R, W>;
+  using S = typename C::S;
+  constexpr int kNibRow = KC * 1024, kScRow = KC * 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
+  unsigned char* const xs = lds + W * C::kStage;
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned char* const sc_stage = lds + wave * C::kStage;
+  unsigned char* const nib_stage = sc_stage + C::kScLoads * 1024;
+  const int row0 = (blockIdx.x * W + wave) * R;
+  const int nrows = max(0, min(R, n - row0));
+
+  // activations: granule t of lane slot i of chunk c lands at c*4096 + t*1024 + 16 i
+  load_shared_pieces<4 * KC, W>(make_rsrc(x, (uint32_t)KC * 4096u), xs, wave, lane, [](int piece, int i) {
+    return (uint32_t)(((piece >> 2) * 256 + i * 4 + (piece & 3)) * 16);
+  });
+  // the scale run, then the first nibble loads
+  const auto sr = make_rsrc(w + (int64_t)n * kNibRow + (int64_t)row0 * kScRow, (uint32_t)(nrows * kScRow));
+  stream_loads<0, C::kScLoads, QGEMV_WLOAD_AUX>(sr, sc_stage, lane);
+  const auto nr = make_rsrc(w + (int64_t)row0 * kNibRow, (uint32_t)(nrows * kNibRow));
+  stream_loads<0, S::issued_before(0), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
+
+  wait_vm<S::issued_before(0)>();  // activations and scales (issued first) are in LDS
+  __builtin_amdgcn_s_barrier();    // ... every wave's activation pieces too
+
+  unsigned X[KC][16];
+#pragma unroll
+  for (int ch = 0; ch < KC; ++ch)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + ch * 4096 + t * 1024 + 16 * lane);
+      X[ch][4 * t] = v.x; X[ch][4 * t + 1] = v.y; X[ch][4 * t + 2] = v.z; X[ch][4 * t + 3] = v.w;
+    }
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  static_for<0, R * KC>([&](auto uc) {
+    constexpr int U = decltype(uc)::value, r = U / KC, ch = U % KC;
+    wait_vm<S::wait_count(U)>();
+    const u32x4 nv = *reinterpret_cast<const u32x4*>(nib_stage + U * 1024 + 16 * lane);
+    const unsigned sc = *reinterpret_cast<const uint16_t*>(sc_stage + U * 128 + 2 * lane);
+    const unsigned q[4] = {nv.x, nv.y, nv.z, nv.w};
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a0 = dot2bf(fp4x2_bf16(q[j >> 2], j), X[ch][j], a0);
+      a1 = dot2bf(fp4x2_bf16(q[2 + (j >> 2)], j), X[ch][8 + j], a1);
+    }
+    const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 0));
+    const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 1));
+    acc[r] = __builtin_fmaf(s1, a1, __builtin_fmaf(s0, a0, acc[r]));
+    // refill: this unit's LDS reads have completed (their data was used above)
+    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
+  });
+  store_rows<R>(acc, y, row0, nrows, 1.f, lane);
+}
+
 // One thread per 16 nibble bytes = 32 weights = two scale blocks.  The
 // flattened [M][K] index of a weight is twice its nibble-byte index (plus the
 // nibble), and its scale is byte (flattened index)/16 of the scale array,
@@ -143,8 +229,43 @@ static hipError_t launch_nvfp4_r(const void* w, const void* x, float* y, int64_t
   return hipGetLastError();
 }
 
+template <int KC, int R, int W>
+static hipError_t launch_nvfp4_rows_r(const void* w, const void* x, float* y, int64_t n, hipStream_t s) {
+  const int64_t rows_per_wg = (int64_t)W * R;
+  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((nvfp4_gemv_rows_kernel<KC, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n);
+  return hipGetLastError();
+}
+
+// Shape -> (R rows per wave, W waves per workgroup), as for Q4_K: up to 1024
+// rows one row per wave and 4 waves; beyond, 8 waves (two per SIMD) and
+// about 256 workgroups; past what one round holds, a smaller stage.
+template <int KC, int RMAX>
+static hipError_t launch_nvfp4_rows(const void* w, const void* x, float* y, int64_t n, hipStream_t s) {
+  const int64_t r8 = (n + 2047) / 2048;
+  if (n <= 1024) return launch_nvfp4_rows_r<KC, 1, 4>(w, x, y, n, s);
+  if (r8 <= 1) return launch_nvfp4_rows_r<KC, 1, 8>(w, x, y, n, s);
+  if (r8 <= 2 || RMAX <= 2) return launch_nvfp4_rows_r<KC, 2, 8>(w, x, y, n, s);
+  if constexpr (RMAX >= 8) {
+    if (r8 <= 4) return launch_nvfp4_rows_r<KC, 4, 8>(w, x, y, n, s);
+    if (r8 <= 7) return launch_nvfp4_rows_r<KC, 7, 8>(w, x, y, n, s);
+    if (r8 <= 8) return launch_nvfp4_rows_r<KC, 8, 8>(w, x, y, n, s);
+    return launch_nvfp4_rows_r<KC, 4, 8>(w, x, y, n, s);
+  }
+  return launch_nvfp4_rows_r<KC, 2, 8>(w, x, y, n, s);
+}
+
+#ifndef QGEMV_NVFP4_IMPL
+#define QGEMV_NVFP4_IMPL 2  // 1: K-split kernel only, 2: row-streaming where instantiated
+#endif
+
 hipError_t launch_nvfp4_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                              hipStream_t s) {
+  if (QGEMV_NVFP4_IMPL == 2 && k % 2048 == 0) {
+    if (k == 14336) return launch_nvfp4_rows<7, 2>(w, x, y, n, s);
+    if (k == 4096) return launch_nvfp4_rows<2, 8>(w, x, y, n, s);
+  }
   return launch_nvfp4_r<QGEMV_NVFP4_R>(w, x, y, n, k, s);
 }
 

@@ -327,7 +327,7 @@ __device__ __forceinline__ constexpr int q4k_xswz(int g) {
 }
 
 #ifndef QGEMV_Q4K_AHEAD
-#define QGEMV_Q4K_AHEAD 6  // weight loads in flight per wave beyond the unit being consumed
+#define QGEMV_Q4K_AHEAD 4  // weight loads in flight per wave beyond the unit being consumed
 #endif
 
 template <int KC, int R, int W>

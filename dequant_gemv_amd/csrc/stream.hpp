@@ -1,0 +1,75 @@
+// Row-streaming skeleton shared by the GEMV kernels: a wave owns whole rows,
+// their bytes are one contiguous run streamed into the wave's LDS stage with
+// 1 KiB buffer loads (lane i of a load fetches bytes 16i..16i+15 of that KiB),
+// the loads are issued on a compile-time schedule that keeps a bounded number
+// in flight ahead of the unit being consumed, and the finished row partials
+// are summed across the wave with DPP and stored by lanes 48.. .
+#pragma once
+#include "device.hpp"
+
+namespace qgemv {
+
+// Schedule of a stream of UNITS units of UNIT_BYTES consecutive bytes (unit u
+// covers bytes [u*UNIT_BYTES, (u+1)*UNIT_BYTES) of the run).  AHEAD0 loads are
+// issued before the first unit is consumed and, after unit u, enough to stay
+// AHEAD loads past the last load unit u depends on.  A CU's memory pipeline
+// holds a bounded number of requests and a wave issuing past that stalls at
+// the load, holding back its own arithmetic: hence the bound.
+template <int UNIT_BYTES, int UNITS, int AHEAD0, int AHEAD>
+struct StreamSchedule {
+  static constexpr int kLoads = (UNITS * UNIT_BYTES + 1023) / 1024;
+  static constexpr int kStage = kLoads * 1024;
+  static_assert(AHEAD >= (UNIT_BYTES + 1023) / 1024 + 1, "lookahead below one unit's loads");
+  static_assert(AHEAD0 >= 1 && AHEAD0 < 60 && AHEAD < 60, "vmcnt holds at most 63 outstanding loads");
+  static constexpr int last_load(int u) { return (u * UNIT_BYTES + UNIT_BYTES - 1) / 1024; }
+  static constexpr int issued_before(int u) {
+    int n = AHEAD0 < kLoads ? AHEAD0 : kLoads;
+    for (int v = 0; v < u; ++v) {
+      const int t = last_load(v) + 1 + AHEAD;
+      n = t > n ? (t < kLoads ? t : kLoads) : n;
+    }
+    return n;
+  }
+  // vmcnt to wait for before consuming unit u (loads complete in issue order)
+  static constexpr int wait_count(int u) { return issued_before(u) - 1 - last_load(u); }
+};
+
+// Issue loads [B, E) of a stream whose LDS stage starts at `stage`.
+template <int B, int E, int AUX>
+__device__ __forceinline__ void stream_loads(__amdgpu_buffer_rsrc_t r, unsigned char* stage, int lane) {
+  static_for<B, E>([&](auto i) {
+    constexpr int I = decltype(i)::value;
+    ld128_lds<AUX>(r, stage + I * 1024, (uint32_t)(I * 1024 + 16 * lane));
+  });
+}
+
+// The workgroup's copy of the activations: PIECES one-KiB pieces dealt to the
+// W waves in turn; lane i of piece P fetches the 16-byte granule src(P, i)
+// (a permutation inside the piece, e.g. a bank swizzle) and stores it at
+// dst + 1024 P + 16 i.  Returns nothing; completion is counted by vmcnt.
+template <int PIECES, int W, typename SrcFn>
+__device__ __forceinline__ void load_shared_pieces(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, int lane,
+                                                   SrcFn src) {
+  constexpr int kPer = (PIECES + W - 1) / W;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int piece = i * W + wave;
+    if (piece < PIECES) ld128_lds(r, dst + piece * 1024, src(piece, lane));
+  }
+}
+
+// Sum R per-lane row partials across the wave and store row j (< nrows) of
+// y[row0 ..] from lane 48 + j, times `scale`.
+template <int R>
+__device__ __forceinline__ void store_rows(float (&acc)[R], float* __restrict__ y, int row0, int nrows, float scale,
+                                           int lane) {
+  static_assert(R >= 1 && R <= 16, "one row per lane of the last 16-lane row");
+  wave_reduce_dpp<R>(acc);
+  const int j = lane & 15;
+  float t = acc[0];
+#pragma unroll
+  for (int s = 1; s < R; ++s) t = j == s ? acc[s] : t;
+  if (lane >= 48 && j < nrows) y[row0 + j] = t * scale;
+}
+
+}  // namespace qgemv

@@ -31,6 +31,7 @@
 // ds_bpermute.  sum x*(t-1) = sum x*t - sum x, the second term precomputed.
 #include "device.hpp"
 #include "launch.hpp"
+#include "stream.hpp"
 
 namespace qgemv {
 
@@ -191,6 +192,134 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void tq1_gemv_kernel(const uin
   }
 }
 
+
+// Row-streaming variant (K a multiple of 4096): a wave owns R whole rows,
+// whose bytes are one contiguous run of R*KS segments of 864 bytes (16 blocks)
+// streamed into the wave's LDS stage with the shared lookahead schedule.
+// Lane l < 54 takes bytes 16l..16l+15 of every segment, as in the K-split
+// kernel; its 8 x 5 activation pairs and per-block-slot sums are read once
+// per segment position from the workgroup's LDS copy of x and reused for all
+// R rows.  The two d values a lane needs are read from the stage; slots whose
+// block lies outside the segment, and lanes past the payload, use d = 0 and
+// zero activations, so they add exactly 0.
+#ifndef QGEMV_TQ1_AHEAD
+#define QGEMV_TQ1_AHEAD 4
+#endif
+
+template <int KS, int R, int W>
+struct Tq1Rows {
+  using S = StreamSchedule<kTq1SegBytes, R * KS, QGEMV_TQ1_AHEAD, QGEMV_TQ1_AHEAD>;
+  static constexpr int kXBytes = KS * 8192;
+  static constexpr int kLds = W * S::kStage + kXBytes + 16;  // + one zero dword: coefficient of a non-element
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+};
+
+template <int KS, int R, int W>
+__global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ x,
+                                                              float* __restrict__ y, int n) {
+  using C = Tq1Rows<KS, R, W>;
+  using S = typename C::S;
+  constexpr int kRowBytes = KS * kTq1SegBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
+  unsigned char* const xs = lds + W * S::kStage;
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned char* const stage = lds + wave * S::kStage;
+  const int row0 = (blockIdx.x * W + wave) * R;
+  const int nrows = max(0, min(R, n - row0));
+
+  load_shared_pieces<8 * KS, W>(make_rsrc(x, (uint32_t)KS * 8192u), xs, wave, lane,
+                                [](int piece, int i) { return (uint32_t)(piece * 1024 + 16 * i); });
+  const auto wr = make_rsrc(w + (int64_t)row0 * kRowBytes, (uint32_t)(nrows * kRowBytes));
+  stream_loads<0, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
+
+  // Lanes past the payload address byte 0 (their results are masked), so every
+  // LDS access below stays inside the wave's own segment or the activations.
+  const bool active = lane < 54;
+  const int o0 = active ? 16 * lane : 0;
+  const int blk0 = o0 / kTq1Bytes;  // the lane's first block in a segment
+  int bnd = 8;                      // byte pairs in the first block
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if ((o0 + 2 * i) / kTq1Bytes != blk0 && bnd == 8) bnd = i;
+  const bool two = active && bnd < 8 && blk0 + 1 < kTq1SegBlocks;  // second slot is a block of the segment
+  const int dof0 = blk0 * kTq1Bytes + 52, dof1 = two ? (blk0 + 1) * kTq1Bytes + 52 : dof0;
+
+  unsigned char* const zero = xs + C::kXBytes;
+  if (wave == 0 && lane == 0) {
+    *reinterpret_cast<unsigned*>(zero) = 0u;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the zero is in LDS before the barrier
+  }
+  wait_vm<S::issued_before(0)>();  // activations (issued first) are in LDS
+  __builtin_amdgcn_s_barrier();    // ... every wave's pieces too
+
+  // Activation pairs of the lane's byte pairs: digit k of payload byte pos
+  // feeds element base + k*stride of its block (qs[0..31]: pos, 32; qs[32..47]:
+  // pos + 128, 16; qh: pos + 192, 4 with no fifth digit); byte pairs past the
+  // payload (d) and lanes past it read the zero dword.  Sums per block slot
+  // use the same snapshot as the units below.
+  unsigned xp[KS][8][5];
+  float xs0[KS], xs1[KS];
+  const unsigned kOnes = 0x3C003C00u;
+  bool last_of_first[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) last_of_first[i] = i == bnd - 1;
+#pragma unroll
+  for (int sg = 0; sg < KS; ++sg) {
+    float a = 0.f, snap = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = o0 + 2 * i;
+      const int blk = o / kTq1Bytes;
+      const int pos = o - blk * kTq1Bytes;
+      const int base = pos < 32 ? pos : pos < 48 ? pos + 128 : pos + 192;
+      const int stride = pos < 32 ? 64 : pos < 48 ? 32 : 8;  // bytes
+      const bool payload = active && pos < 52;
+      const unsigned char* p0 = payload ? xs + sg * 8192 + (blk * 256 + base) * 2 : zero;
+      const int st = payload ? stride : 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xp[sg][i][k] = *reinterpret_cast<const unsigned*>(p0 + k * st);
+      xp[sg][i][4] = *reinterpret_cast<const unsigned*>(pos < 48 ? p0 + 4 * st : zero);
+#pragma unroll
+      for (int k = 0; k < 5; ++k) a = dot2h(xp[sg][i][k], kOnes, a);
+      snap = last_of_first[i] ? a : snap;
+    }
+    xs0[sg] = snap;
+    xs1[sg] = a - snap;
+  }
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  static_for<0, R * KS>([&](auto uc) {
+    constexpr int U = decltype(uc)::value, r = U / KS, sg = U % KS;
+    wait_vm<S::wait_count(U)>();
+    const unsigned char* seg = stage + U * kTq1SegBytes;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(seg + o0);
+    const unsigned short db0 = *reinterpret_cast<const unsigned short*>(seg + dof0);
+    const unsigned short db1 = *reinterpret_cast<const unsigned short*>(seg + dof1);
+    const float d0 = active ? (float)__builtin_bit_cast(_Float16, db0) : 0.f;
+    const float d1 = two ? (float)__builtin_bit_cast(_Float16, db1) : 0.f;
+    const unsigned dw[4] = {raw.x, raw.y, raw.z, raw.w};
+    float a = 0.f, snap = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned B = __builtin_amdgcn_perm(0u, dw[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
+      unsigned D[5];
+      tq1_digits(B, D);
+#pragma unroll
+      for (int k = 0; k < 5; ++k) a = dot2h(D[k], xp[sg][i][k], a);
+      snap = last_of_first[i] ? a : snap;
+    }
+    const float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0[sg]), acc[r]);
+    acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1[sg]), t);
+    // refill: this unit's LDS reads have completed (their data was used above)
+    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(wr, stage, lane);
+  });
+  store_rows<R>(acc, y, row0, nrows, 1.f, lane);
+}
+
 // One thread per (block, run of 16 elements il): elements 16 il .. 16 il + 15.
 // For il < 10 they are digit il/2 of qs[16 (il%2) + e]; for il < 15 digit
 // il-10 of qs[32 + e]; il = 15 is digit e/4 of qh[e%4] (the section-2 element
@@ -237,8 +366,32 @@ static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n
   return hipGetLastError();
 }
 
+template <int KS, int R, int W>
+static hipError_t launch_tq1_rows_r(const void* w, const void* x, float* y, int64_t n, hipStream_t s) {
+  const int64_t rows_per_wg = (int64_t)W * R;
+  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((tq1_gemv_rows_kernel<KS, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n);
+  return hipGetLastError();
+}
+
+#ifndef QGEMV_TQ1_IMPL
+#define QGEMV_TQ1_IMPL 2  // 1: K-split kernel only, 2: row-streaming where instantiated
+#endif
+
+// Shape -> (R rows per wave, W waves per workgroup), as for Q4_K.
 hipError_t launch_tq1_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                            hipStream_t s) {
+  if (QGEMV_TQ1_IMPL == 2 && k == 4096) {
+    const int64_t r8 = (n + 2047) / 2048;
+    if (n <= 1024) return launch_tq1_rows_r<1, 1, 4>(w, x, y, n, s);
+    if (r8 <= 1) return launch_tq1_rows_r<1, 1, 8>(w, x, y, n, s);
+    if (r8 <= 2) return launch_tq1_rows_r<1, 2, 8>(w, x, y, n, s);
+    if (r8 <= 4) return launch_tq1_rows_r<1, 4, 8>(w, x, y, n, s);
+    if (r8 <= 7) return launch_tq1_rows_r<1, 7, 8>(w, x, y, n, s);
+    if (r8 <= 8) return launch_tq1_rows_r<1, 8, 8>(w, x, y, n, s);
+    return launch_tq1_rows_r<1, 8, 8>(w, x, y, n, s);
+  }
   return launch_tq1_r<QGEMV_TQ1_R>(w, x, y, n, k, s);
 }
 

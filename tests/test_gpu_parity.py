@@ -142,6 +142,18 @@ def test_gemv_small(q, fmt, n, k):
     _check_gemv(q, fmt, n, k, seed=n + k)
 
 
+# Every rows-per-wave / waves-per-workgroup choice of the row-streaming
+# kernels (the shape decides it), with ragged last workgroups.
+ROW_STREAM = [(fmt, n, k) for fmt in ("nvfp4", "tq1") for n, k in (
+    (1500, 4096), (3000, 4096), (5000, 4096), (14336, 4096), (16000, 4096))] + [
+    ("nvfp4", 1500, 14336), ("nvfp4", 5000, 14336)]
+
+
+@pytest.mark.parametrize("fmt,n,k", ROW_STREAM)
+def test_gemv_row_stream_shapes(q, fmt, n, k):
+    _check_gemv(q, fmt, n, k, seed=7 * n + k, sample=1500)
+
+
 FULL = [
     # the decode shapes: Q4_K 4096x4096, Q4_K gate/up 14336x4096 and down
     # 4096x14336, NVFP4 4096x14336, TQ1_0 14336x4096; every row checked
