@@ -1,5 +1,6 @@
-// Pure-read bandwidth probe: the same coalesced dwordx4 buffer loads as the
-// GEMV kernels over a given byte range, folded with xor so nothing is elided.
+// Pure-read bandwidth probe: the same coalesced dwordx4 buffer loads (with the
+// same non-temporal hint) as the GEMV weight streams over a given byte range,
+// folded with xor so nothing is elided.
 // It measures what the part delivers for a read-once stream of that size.
 #include "device.hpp"
 #include "launch.hpp"
@@ -20,7 +21,7 @@ __global__ __launch_bounds__(kCeilThreads) void read_ceiling_kernel(const uint8_
   u32x4 v[kCeilLoads];
 #pragma unroll
   for (int u = 0; u < kCeilLoads; ++u)
-    v[u] = ld128(r, (uint32_t)((u * kCeilThreads + threadIdx.x) * 16));
+    v[u] = ld128w(r, (uint32_t)((u * kCeilThreads + threadIdx.x) * 16));
   unsigned acc = 0;
 #pragma unroll
   for (int u = 0; u < kCeilLoads; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;

@@ -27,13 +27,11 @@
 // wave_reduce_rows) and across the K-chunk waves through LDS.
 #include "device.hpp"
 #include "launch.hpp"
+#include "stream.hpp"
 
 namespace qgemv {
 
-// Rows per wave and waves per workgroup (tuning).
-#ifndef QGEMV_Q4K_R
-#define QGEMV_Q4K_R 8
-#endif
+// Waves per workgroup of the K-split kernel (tuning).
 #ifndef QGEMV_WG_WAVES
 #define QGEMV_WG_WAVES 8
 #endif
@@ -65,113 +63,7 @@ struct Q4kScaleSel {
   }
 };
 
-template <int R>
-__global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void q4k_gemv_kernel(const uint8_t* __restrict__ w,
-                                                       const uint16_t* __restrict__ x,
-                                                       float* __restrict__ y, int n, int nb,
-                                                       int kc, int kw, int rg) {
-  __shared__ float red[16 * 16];
-  const int lane = __lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer descriptors in SGPRs
-  const int kwi = wave % kw;
-  const int rgi = wave / kw;
-  const int64_t row_bytes = (int64_t)nb * kQ4kBytes;
-  const int row0 = blockIdx.x * rg * R + rgi * R;
-  const int nrows = max(0, min(R, n - row0));
-  const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, (uint32_t)(nrows * row_bytes));
-  const auto xr = make_rsrc(x, (uint32_t)nb * 512u);
-
-  const int bl = lane >> 3, p = lane & 7, c = p >> 1, h = p & 1;
-  const Q4kScaleSel sel(c);
-  const unsigned kOnes = 0x3C003C00u;  // fp16 (1, 1)
-
-  float acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-
-  for (int ch = kwi; ch < kc; ch += kw) {
-    const int b = ch * 8 + bl;
-    // Lanes past the last block of a ragged chunk point at the end of the
-    // range: their loads read zeros (d = dmin = q = 0) and add exactly 0, so
-    // no lane needs a branch or a select around the loaded data.
-    const uint32_t lane_off = b < nb ? (uint32_t)(b * kQ4kBytes) : (uint32_t)(nrows * row_bytes);
-    // The lane's 32 activations (16 of group 2c, 16 of group 2c+1) are loaded
-    // first: loads complete in issue order, so the rows below can be consumed
-    // one by one as they arrive instead of after the whole batch.
-    const uint32_t xo = (uint32_t)(b * 256 + 64 * c + 16 * h) * 2u;
-    const u32x4 xa0 = ld128(xr, xo), xa1 = ld128(xr, xo + 16);
-    const u32x4 xb0 = ld128(xr, xo + 64), xb1 = ld128(xr, xo + 80);
-    // Then the weights of all R rows, all in flight at once.
-    u32x4 hdr[R], qs[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t off = lane_off + (uint32_t)(r * row_bytes);
-      hdr[r] = ld128w(wr, off);
-      qs[r] = ld128w(wr, off + 16 + 16 * p);
-    }
-    const unsigned XA[8] = {xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
-    const unsigned XB[8] = {xb0.x, xb0.y, xb0.z, xb0.w, xb1.x, xb1.y, xb1.z, xb1.w};
-    // Pairs (x[4t], x[4t+2]) and (x[4t+1], x[4t+3]) match the two fp16 halves
-    // of a nibble dword masked with 0x000F000F / 0x00F000F0 (bytes 0 and 2)
-    // and the same after >> 8 (bytes 1 and 3).
-    unsigned pa02[4], pa13[4], pb02[4], pb13[4];
-    float sxa = 0.f, sxb = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pa02[t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x05040100u);
-      pa13[t] = __builtin_amdgcn_perm(XA[2 * t + 1], XA[2 * t], 0x07060302u);
-      pb02[t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x05040100u);
-      pb13[t] = __builtin_amdgcn_perm(XB[2 * t + 1], XB[2 * t], 0x07060302u);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sxa = dot2h(XA[i], kOnes, sxa);
-      sxb = dot2h(XB[i], kOnes, sxb);
-    }
-    // X_g * 2^-24, to meet Q_g * 2^-24 from the subnormal nibbles.
-    sxa *= 0x1p-24f;
-    sxb *= 0x1p-24f;
-
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const unsigned q[4] = {qs[r].x, qs[r].y, qs[r].z, qs[r].w};
-      float qa = 0.f, qb = 0.f;  // 2^-24 Q_a, 2^-20 Q_b
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const unsigned w0 = q[t], w8 = q[t] >> 8;
-        qa = dot2h(w0 & 0x000F000Fu, pa02[t], qa);
-        qa = dot2h(w8 & 0x000F000Fu, pa13[t], qa);
-        qb = dot2h(w0 & 0x00F000F0u, pb02[t], qb);
-        qb = dot2h(w8 & 0x00F000F0u, pb13[t], qb);
-      }
-      const unsigned sp = sel.scales(hdr[r].y, hdr[r].w);
-      const unsigned mp = sel.mins(hdr[r].z, hdr[r].w);
-      const float sa = (float)(sp & 0xFFu), sb = (float)((sp >> 8) & 0xFFu);
-      const float ma = (float)(mp & 0xFFu), mb = (float)((mp >> 8) & 0xFFu);
-      const float d = f16lo(hdr[r].x), dmin = f16hi(hdr[r].x);
-      const float v = __builtin_fmaf(sb, qb * 0.0625f, sa * qa);
-      const float mx = __builtin_fmaf(mb, sxb, ma * sxa);
-      acc[r] = __builtin_fmaf(-dmin, mx, __builtin_fmaf(d, v, acc[r]));
-    }
-  }
-
-  wave_reduce_rows<R>(acc);
-  constexpr int L = log2i<R>();
-  constexpr int kLanesPerRow = 64 >> L;
-  if ((lane & (kLanesPerRow - 1)) == 0)
-    red[(rgi * kw + kwi) * R + (lane >> (6 - L))] = acc[0];
-  __syncthreads();
-  const int t = threadIdx.x;
-  if (t < rg * R) {
-    const int g = t / R, r = t % R;
-    float s = 0.f;
-    for (int k = 0; k < kw; ++k) s += red[(g * kw + k) * R + r];
-    const int row = blockIdx.x * rg * R + g * R + r;
-    if (row < n) y[row] = s * 0x1p24f;
-  }
-}
-
-// LDS-transposed variant of the GEMV above.  A wave owns one K-chunk of 8
+// K-split GEMV (any K).  A wave owns one K-chunk of 8
 // blocks for a batch of 8 rows: 8 x 1152 contiguous-per-row bytes = 9 KiB,
 // read with nine dwordx4 loads of one 16-byte piece per lane.  Every load is
 // one 1 KiB run starting on a 128-byte line (1152 = 9*128 and a row of a
@@ -332,30 +224,14 @@ __device__ __forceinline__ constexpr int q4k_xswz(int g) {
 
 template <int KC, int R, int W>
 struct Q4kRows {
-  static constexpr int kUnitBytes = 8 * kQ4kBytes;                        // 1152
-  static constexpr int kLoads = (R * KC * kUnitBytes + 1023) / 1024;      // weight loads per wave
-  static constexpr int kStage = kLoads * 1024;                            // LDS bytes per wave
-  static constexpr int kXBytes = KC * 4096;                               // activations in LDS
-  static constexpr int kLds = W * kStage + kXBytes;
-  static constexpr int kXLoads = (4 * KC + W - 1) / W;                    // activation loads per wave (at most)
+  static constexpr int kUnitBytes = 8 * kQ4kBytes;  // 1152
+  // Unit u = r*KC + ch; the schedule assumes the largest row record (8*KC
+  // blocks), shorter records only end earlier.
+  using S = StreamSchedule<kUnitBytes, R * KC, QGEMV_Q4K_AHEAD, QGEMV_Q4K_AHEAD>;
+  static constexpr int kXBytes = KC * 4096;  // activations in LDS
+  static constexpr int kLds = W * S::kStage + kXBytes;
   static_assert(KC >= 1 && KC <= 8, "K-chunk count");
-  static_assert(KC + kLoads < 64, "vmcnt holds at most 63 outstanding loads");
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
-  // Last load unit u (= r*KC + ch) can depend on, for the largest row record
-  // (8*KC blocks; shorter records only end earlier).
-  static constexpr int last_load(int u) { return (u * kUnitBytes + kUnitBytes - 1) / 1024; }
-  // Weight loads issued before unit u is consumed: the first kAhead up front,
-  // then after each unit enough to stay kAhead loads past it.
-  static constexpr int kAhead = QGEMV_Q4K_AHEAD;
-  static_assert(kAhead >= 2, "a unit spans up to two loads");
-  static constexpr int issued_before(int u) {
-    int n = kAhead < kLoads ? kAhead : kLoads;
-    for (int v = 0; v < u; ++v) {
-      const int t = last_load(v) + 1 + kAhead;
-      n = t > n ? (t < kLoads ? t : kLoads) : n;
-    }
-    return n;
-  }
 };
 
 template <int KC, int R, int W>
@@ -363,38 +239,29 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
                                                                       const uint16_t* __restrict__ x,
                                                                       float* __restrict__ y, int n, int nb) {
   using C = Q4kRows<KC, R, W>;
+  using S = typename C::S;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
-  unsigned char* const xs = lds + W * C::kStage;
+  unsigned char* const xs = lds + W * S::kStage;
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  unsigned char* const stage = lds + wave * C::kStage;
+  unsigned char* const stage = lds + wave * S::kStage;
   const int row_bytes = nb * kQ4kBytes;
   const int row0 = (blockIdx.x * W + wave) * R;
   const int nrows = max(0, min(R, n - row0));
 
-  // Activations first: the workgroup's 4*KC one-KiB pieces, dealt to the
-  // waves in turn.
-  {
-    const auto xr = make_rsrc(x, (uint32_t)nb * 512u);
-    const int g = lane & 31;
-    const uint32_t src = (uint32_t)((lane & 32) + q4k_xswz(g)) * 16u;
-#pragma unroll
-    for (int i = 0; i < C::kXLoads; ++i) {
-      const int piece = i * W + wave;
-      if (piece < 4 * KC) ld128_lds(xr, xs + piece * 1024, (uint32_t)piece * 1024u + src);
-    }
-  }
-  // Then the first weight loads of the wave's rows.
-  const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, (uint32_t)(nrows * row_bytes));
-  static_for<0, C::issued_before(0)>([&](auto i) {
-    ld128_lds<QGEMV_WLOAD_AUX>(wr, stage + decltype(i)::value * 1024, (uint32_t)(decltype(i)::value * 1024 + 16 * lane));
+  // Activations first (the workgroup's 4*KC one-KiB pieces, swizzled), then
+  // the first weight loads of the wave's rows.
+  load_shared_pieces<4 * KC, W>(make_rsrc(x, (uint32_t)nb * 512u), xs, wave, lane, [](int piece, int i) {
+    return (uint32_t)(piece * 1024 + ((i & 32) + q4k_xswz(i & 31)) * 16);
   });
+  const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, (uint32_t)(nrows * row_bytes));
+  stream_loads<0, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
 
   const int bl = lane >> 3, p = lane & 7, c = p >> 1, h = p & 1;
   const Q4kScaleSel sel(c);
   const unsigned kOnes = 0x3C003C00u;
 
-  wait_vm<C::issued_before(0)>();  // this wave's activation pieces (issued before the weights) are in LDS
+  wait_vm<S::issued_before(0)>();  // this wave's activation pieces (issued before the weights) are in LDS
   __builtin_amdgcn_s_barrier();  // ... and every other wave's
 
   // The lane's activations for every chunk, as fp16 pairs matching the masked
@@ -438,7 +305,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
   static_for<0, R * KC>([&](auto u) {
     constexpr int U = decltype(u)::value, r = U / KC, ch = U % KC;
-    wait_vm<C::issued_before(U) - 1 - C::last_load(U)>();
+    wait_vm<S::wait_count(U)>();
     const unsigned char* blk = stage + r * row_bytes + ch * C::kUnitBytes + bl * kQ4kBytes;
     const u32x4 hdr = *reinterpret_cast<const u32x4*>(blk);
     const u32x4 qv = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * p);
@@ -465,17 +332,9 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
     else
       acc[r] += part;
     // refill: this unit's LDS reads have completed (their data was used above)
-    static_for<C::issued_before(U), C::issued_before(U + 1)>([&](auto i) {
-      ld128_lds<QGEMV_WLOAD_AUX>(wr, stage + decltype(i)::value * 1024, (uint32_t)(decltype(i)::value * 1024 + 16 * lane));
-    });
+    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(wr, stage, lane);
   });
-
-  wave_reduce_dpp<R>(acc);
-  const int j = lane & 15;
-  float t = acc[0];
-#pragma unroll
-  for (int s = 1; s < R; ++s) t = j == s ? acc[s] : t;
-  if (lane >= 48 && j < nrows) y[row0 + j] = t * 0x1p24f;
+  store_rows<R>(acc, y, row0, nrows, 0x1p24f, lane);
 }
 
 // One thread per (block, 16-byte nibble slice): 32 weights, written as the
@@ -509,20 +368,6 @@ __global__ __launch_bounds__(256) void q4k_dequant_kernel(const uint8_t* __restr
     *reinterpret_cast<float4*>(o + j) = make_float4(lo[j], lo[j + 1], lo[j + 2], lo[j + 3]);
     *reinterpret_cast<float4*>(o + 32 + j) = make_float4(hi[j], hi[j + 1], hi[j + 2], hi[j + 3]);
   }
-}
-
-template <int R>
-static hipError_t launch_q4k_r(const void* w, const void* x, float* y, int64_t n, int64_t k,
-                               hipStream_t s) {
-  const int nb = (int)(k / 256);
-  const int kc = (nb + 7) / 8;
-  const int kw = kc < QGEMV_WG_WAVES ? kc : QGEMV_WG_WAVES;
-  const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
-  const int rows_per_wg = rg * R;
-  const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(q4k_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
-                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, nb, kc, kw, rg);
-  return hipGetLastError();
 }
 
 static hipError_t launch_q4k_lds(const void* w, const void* x, float* y, int64_t n, int64_t k,
@@ -581,8 +426,7 @@ static bool launch_q4k_rows(const void* w, const void* x, float* y, int64_t n, i
   return false;
 }
 
-// 0: register-staged kernel, 1: LDS-staged K-split kernel, 2: row-streaming
-// kernel where instantiated (K-split otherwise)
+// 1: K-split kernel only, 2: row-streaming kernel where instantiated (K-split otherwise)
 #ifndef QGEMV_Q4K_IMPL
 #define QGEMV_Q4K_IMPL 2
 #endif
@@ -593,8 +437,7 @@ hipError_t launch_q4k_gemv(const void* w, const void* x, float* y, int64_t n, in
     hipError_t e = hipSuccess;
     if (launch_q4k_rows(w, x, y, n, k, s, &e)) return e;
   }
-  if (QGEMV_Q4K_IMPL >= 1) return launch_q4k_lds(w, x, y, n, k, s);
-  return launch_q4k_r<QGEMV_Q4K_R>(w, x, y, n, k, s);
+  return launch_q4k_lds(w, x, y, n, k, s);
 }
 
 hipError_t launch_q4k_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
