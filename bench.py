@@ -90,7 +90,7 @@ def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
         fn(ws[i % rotate], x, y, n, k, s_handle)
 
     with torch.cuda.stream(stream):
-        for i in range(warmup):
+        for i in range(rotate):  # first touch of every copy
             one(i)
     torch.cuda.synchronize()
 
@@ -101,7 +101,16 @@ def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
             for i in range(rotate):
                 one(i)
         torch.cuda.synchronize()
-        graph.replay()  # one untimed replay
+        # the untimed warm-up steps, as replays of the same graph right before
+        # the timed region (the GPU leaves its idle state before timing starts)
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, warmup // rotate)):
+                graph.replay()
+        torch.cuda.synchronize()
+    else:
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                one(i)
         torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -137,12 +146,16 @@ def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
         sink = torch.empty(qgemv.qgemv_read_sink_len(wb), dtype=torch.float32, device=dev)
         cg = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
-            for i in range(warmup):
-                qgemv.qgemv_read_ceiling(ws[i % rotate], wb, sink, s_handle)
+            for i in range(rotate):
+                qgemv.qgemv_read_ceiling(ws[i], wb, sink, s_handle)
         torch.cuda.synchronize()
         with torch.cuda.graph(cg, stream=stream):
             for i in range(rotate):
                 qgemv.qgemv_read_ceiling(ws[i], wb, sink, s_handle)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, warmup // rotate)):
+                cg.replay()
         reps = max(1, steps // rotate)
         torch.cuda.synchronize()
         ev0.record(stream)
@@ -197,7 +210,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3200)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=1280)
     ap.add_argument("--rotate", type=int, default=32, help="distinct weight copies cycled through")
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-extra", action="store_true", help="skip the other formats' shapes")

@@ -116,10 +116,13 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void nvfp4_gemv_kernel(const u
 #ifndef QGEMV_NVFP4_AHEAD
 #define QGEMV_NVFP4_AHEAD 4
 #endif
+#ifndef QGEMV_NVFP4_FIRST
+#define QGEMV_NVFP4_FIRST QGEMV_NVFP4_AHEAD
+#endif
 
 template <int KC, int R, int W>
 struct Nvfp4Rows {
-  using S = StreamSchedule<1024, R * KC, QGEMV_NVFP4_AHEAD, QGEMV_NVFP4_AHEAD>;
+  using S = StreamSchedule<1024, R * KC, QGEMV_NVFP4_AHEAD, QGEMV_NVFP4_AHEAD, QGEMV_NVFP4_FIRST>;
   static constexpr int kScLoads = (R * KC * 128 + 1023) / 1024;
   static constexpr int kStage = kScLoads * 1024 + S::kStage;
   static constexpr int kLds = W * kStage + KC * 4096;
@@ -150,10 +153,11 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
   const auto sr = make_rsrc(w + (int64_t)n * kNibRow + (int64_t)row0 * kScRow, (uint32_t)(nrows * kScRow));
   stream_loads<0, C::kScLoads, QGEMV_WLOAD_AUX>(sr, sc_stage, lane);
   const auto nr = make_rsrc(w + (int64_t)row0 * kNibRow, (uint32_t)(nrows * kNibRow));
-  stream_loads<0, S::issued_before(0), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
+  stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
 
-  wait_vm<S::issued_before(0)>();  // activations and scales (issued first) are in LDS
-  __builtin_amdgcn_s_barrier();    // ... every wave's activation pieces too
+  wait_vm<S::kUpFront>();        // activations and scales (issued first) are in LDS
+  __builtin_amdgcn_s_barrier();  // ... every wave's activation pieces too
+  stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
 
   unsigned X[KC][16];
 #pragma unroll

@@ -11,19 +11,22 @@ namespace qgemv {
 
 // Schedule of a stream of UNITS units of UNIT_BYTES consecutive bytes (unit u
 // covers bytes [u*UNIT_BYTES, (u+1)*UNIT_BYTES) of the run).  AHEAD0 loads are
-// issued before the first unit is consumed and, after unit u, enough to stay
-// AHEAD loads past the last load unit u depends on.  A CU's memory pipeline
-// holds a bounded number of requests and a wave issuing past that stalls at
-// the load, holding back its own arithmetic: hence the bound.
-template <int UNIT_BYTES, int UNITS, int AHEAD0, int AHEAD>
+// issued up front (before the kernel's activation barrier), FIRST - AHEAD0
+// more right after it (they keep the memory pipe fed while the activations
+// are unpacked), and after unit u enough to stay AHEAD loads past the last
+// load unit u depends on.  A CU's memory pipeline holds a bounded number of
+// requests and a wave issuing past that stalls at the load, holding back its
+// own arithmetic (and the barrier): hence the bounds.
+template <int UNIT_BYTES, int UNITS, int AHEAD0, int AHEAD, int FIRST = AHEAD0>
 struct StreamSchedule {
   static constexpr int kLoads = (UNITS * UNIT_BYTES + 1023) / 1024;
   static constexpr int kStage = kLoads * 1024;
   static_assert(AHEAD >= (UNIT_BYTES + 1023) / 1024 + 1, "lookahead below one unit's loads");
-  static_assert(AHEAD0 >= 1 && AHEAD0 < 60 && AHEAD < 60, "vmcnt holds at most 63 outstanding loads");
+  static_assert(AHEAD0 >= 1 && FIRST >= AHEAD0 && FIRST < 60 && AHEAD < 60, "vmcnt holds at most 63 outstanding loads");
+  static constexpr int kUpFront = AHEAD0 < kLoads ? AHEAD0 : kLoads;  // issued before the barrier
   static constexpr int last_load(int u) { return (u * UNIT_BYTES + UNIT_BYTES - 1) / 1024; }
   static constexpr int issued_before(int u) {
-    int n = AHEAD0 < kLoads ? AHEAD0 : kLoads;
+    int n = FIRST < kLoads ? FIRST : kLoads;
     for (int v = 0; v < u; ++v) {
       const int t = last_load(v) + 1 + AHEAD;
       n = t > n ? (t < kLoads ? t : kLoads) : n;

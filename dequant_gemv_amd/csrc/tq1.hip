@@ -205,10 +205,13 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void tq1_gemv_kernel(const uin
 #ifndef QGEMV_TQ1_AHEAD
 #define QGEMV_TQ1_AHEAD 4
 #endif
+#ifndef QGEMV_TQ1_FIRST
+#define QGEMV_TQ1_FIRST QGEMV_TQ1_AHEAD
+#endif
 
 template <int KS, int R, int W>
 struct Tq1Rows {
-  using S = StreamSchedule<kTq1SegBytes, R * KS, QGEMV_TQ1_AHEAD, QGEMV_TQ1_AHEAD>;
+  using S = StreamSchedule<kTq1SegBytes, R * KS, QGEMV_TQ1_AHEAD, QGEMV_TQ1_AHEAD, QGEMV_TQ1_FIRST>;
   static constexpr int kXBytes = KS * 8192;
   static constexpr int kLds = W * S::kStage + kXBytes + 16;  // + one zero dword: coefficient of a non-element
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   load_shared_pieces<8 * KS, W>(make_rsrc(x, (uint32_t)KS * 8192u), xs, wave, lane,
                                 [](int piece, int i) { return (uint32_t)(piece * 1024 + 16 * i); });
   const auto wr = make_rsrc(w + (int64_t)row0 * kRowBytes, (uint32_t)(nrows * kRowBytes));
-  stream_loads<0, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
+  stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX>(wr, stage, lane);
 
   // Lanes past the payload address byte 0 (their results are masked), so every
   // LDS access below stays inside the wave's own segment or the activations.
@@ -251,8 +254,9 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
     *reinterpret_cast<unsigned*>(zero) = 0u;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the zero is in LDS before the barrier
   }
-  wait_vm<S::issued_before(0)>();  // activations (issued first) are in LDS
-  __builtin_amdgcn_s_barrier();    // ... every wave's pieces too
+  wait_vm<S::kUpFront>();        // activations (issued first) are in LDS
+  __builtin_amdgcn_s_barrier();  // ... every wave's pieces too
+  stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
 
   // Activation pairs of the lane's byte pairs: digit k of payload byte pos
   // feeds element base + k*stride of its block (qs[0..31]: pos, 32; qs[32..47]:
