@@ -104,10 +104,10 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void nvfp4_gemv_kernel(const u
 }
 
 
-// Row-streaming variant (K a multiple of 2048): a wave owns R whole rows.
-// Its nibbles are one contiguous run of R*K/2 bytes in which unit u = r*KC +
-// ch (row r, K-chunk ch of 2048 weights) is exactly load u; its scales are a
-// second run of R*K/16 bytes, loaded up front.  Both land in the wave's LDS
+// Row-streaming variant (K <= 16384): a wave owns R whole rows.  Its nibbles
+// are one contiguous run of R*K/2 bytes in which unit u = r*KC + ch (row r,
+// K-chunk ch of up to 2048 weights) starts at r*K/2 + 1024 ch; its scales are
+// a second run of R*K/16 bytes, loaded up front.  Both land in the wave's LDS
 // stage.  The activations are copied once per workgroup into LDS with each
 // 64-byte lane slice spread as four 16-byte granules 1 KiB apart (so each of
 // a lane's four reads is one contiguous 1 KiB across the wave) and held in
@@ -132,10 +132,10 @@ struct Nvfp4Rows {
 template <int KC, int R, int W>
 __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* __restrict__ w,
                                                                 const uint16_t* __restrict__ x,
-                                                                float* __restrict__ y, int n) {
+                                                                float* __restrict__ y, int n, int k) {
   using C = Nvfp4Rows<KC, R, W>;
-  using S = typename C::S;
-  constexpr int kNibRow = KC * 1024, kScRow = KC * 128;
+  using S = typename C::S;  // assumes the longest rows (K = 2048 KC); shorter rows only end earlier
+  const int kNibRow = k / 2, kScRow = k / 16;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
   unsigned char* const xs = lds + W * C::kStage;
   const int lane = __lane_id();
@@ -146,16 +146,24 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
   const int nrows = max(0, min(R, n - row0));
 
   // activations: granule t of lane slot i of chunk c lands at c*4096 + t*1024 + 16 i
-  load_shared_pieces<4 * KC, W>(make_rsrc(x, (uint32_t)KC * 4096u), xs, wave, lane, [](int piece, int i) {
+  load_shared_pieces<4 * KC, W>(make_rsrc(x, (uint32_t)k * 2u), xs, wave, lane, [](int piece, int i) {
     return (uint32_t)(((piece >> 2) * 256 + i * 4 + (piece & 3)) * 16);
   });
-  // the scale run, then the first nibble loads
-  const auto sr = make_rsrc(w + (int64_t)n * kNibRow + (int64_t)row0 * kScRow, (uint32_t)(nrows * kScRow));
+  // The scale run, then the first nibble loads.  The run is nrows*K/16
+  // bytes, not always a multiple of 16, and a 16-byte load that crosses the
+  // end of the range reads as zero: its last 2..14 bytes are fetched again
+  // with exact 2-byte loads and written over the zeros once the piece is in.
+  const uint32_t sc_len = (uint32_t)(nrows * kScRow);
+  const uint32_t sc_full = sc_len & ~15u;
+  const bool tail_lane = 2u * (uint32_t)lane < sc_len - sc_full;
+  const auto sr = make_rsrc(w + (int64_t)n * kNibRow + (int64_t)row0 * kScRow, sc_len);
   stream_loads<0, C::kScLoads, QGEMV_WLOAD_AUX>(sr, sc_stage, lane);
+  const unsigned short sc_tail = ld16(sr, tail_lane ? sc_full + 2u * lane : sc_len);
   const auto nr = make_rsrc(w + (int64_t)row0 * kNibRow, (uint32_t)(nrows * kNibRow));
   stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
 
-  wait_vm<S::kUpFront>();        // activations and scales (issued first) are in LDS
+  wait_vm<S::kUpFront>();  // activations, scales and the scale tail (issued first) are in
+  if (tail_lane) *reinterpret_cast<unsigned short*>(sc_stage + sc_full + 2 * lane) = sc_tail;
   __builtin_amdgcn_s_barrier();  // ... every wave's activation pieces too
   stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
 
@@ -168,14 +176,17 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
       X[ch][4 * t] = v.x; X[ch][4 * t + 1] = v.y; X[ch][4 * t + 2] = v.z; X[ch][4 * t + 3] = v.w;
     }
 
+  // lanes past K in a ragged last chunk: the next row's bytes meet zero
+  // activations, and their scales are dropped (a NaN scale must not leak)
+  const bool tail_ok = (KC - 1) * 2048 + 32 * lane < k;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
   static_for<0, R * KC>([&](auto uc) {
     constexpr int U = decltype(uc)::value, r = U / KC, ch = U % KC;
     wait_vm<S::wait_count(U)>();
-    const u32x4 nv = *reinterpret_cast<const u32x4*>(nib_stage + U * 1024 + 16 * lane);
-    const unsigned sc = *reinterpret_cast<const uint16_t*>(sc_stage + U * 128 + 2 * lane);
+    const u32x4 nv = *reinterpret_cast<const u32x4*>(nib_stage + r * kNibRow + ch * 1024 + 16 * lane);
+    const unsigned sc = *reinterpret_cast<const uint16_t*>(sc_stage + r * kScRow + ch * 128 + 2 * lane);
     const unsigned q[4] = {nv.x, nv.y, nv.z, nv.w};
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -183,8 +194,12 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
       a0 = dot2bf(fp4x2_bf16(q[j >> 2], j), X[ch][j], a0);
       a1 = dot2bf(fp4x2_bf16(q[2 + (j >> 2)], j), X[ch][8 + j], a1);
     }
-    const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 0));
-    const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 1));
+    float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 0));
+    float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 1));
+    if constexpr (ch == KC - 1) {
+      s0 = tail_ok ? s0 : 0.f;
+      s1 = tail_ok ? s1 : 0.f;
+    }
     acc[r] = __builtin_fmaf(s1, a1, __builtin_fmaf(s0, a0, acc[r]));
     // refill: this unit's LDS reads have completed (their data was used above)
     stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
@@ -234,41 +249,42 @@ static hipError_t launch_nvfp4_r(const void* w, const void* x, float* y, int64_t
 }
 
 template <int KC, int R, int W>
-static hipError_t launch_nvfp4_rows_r(const void* w, const void* x, float* y, int64_t n, hipStream_t s) {
+static hipError_t launch_nvfp4_rows_r(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
   const int64_t rows_per_wg = (int64_t)W * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL((nvfp4_gemv_rows_kernel<KC, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
-                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n);
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)k);
   return hipGetLastError();
 }
 
-// Shape -> (R rows per wave, W waves per workgroup), as for Q4_K: up to 1024
-// rows one row per wave and 4 waves; beyond, 8 waves (two per SIMD) and
-// about 256 workgroups; past what one round holds, a smaller stage.
-template <int KC, int RMAX>
-static hipError_t launch_nvfp4_rows(const void* w, const void* x, float* y, int64_t n, hipStream_t s) {
-  const int64_t r8 = (n + 2047) / 2048;
-  if (n <= 1024) return launch_nvfp4_rows_r<KC, 1, 4>(w, x, y, n, s);
-  if (r8 <= 1) return launch_nvfp4_rows_r<KC, 1, 8>(w, x, y, n, s);
-  if (r8 <= 2 || RMAX <= 2) return launch_nvfp4_rows_r<KC, 2, 8>(w, x, y, n, s);
-  if constexpr (RMAX >= 8) {
-    if (r8 <= 4) return launch_nvfp4_rows_r<KC, 4, 8>(w, x, y, n, s);
-    if (r8 <= 7) return launch_nvfp4_rows_r<KC, 7, 8>(w, x, y, n, s);
-    if (r8 <= 8) return launch_nvfp4_rows_r<KC, 8, 8>(w, x, y, n, s);
-    return launch_nvfp4_rows_r<KC, 4, 8>(w, x, y, n, s);
-  }
-  return launch_nvfp4_rows_r<KC, 2, 8>(w, x, y, n, s);
+template <int KC>
+static hipError_t launch_nvfp4_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+  constexpr int kRmax = largest_fitting_r([](int r) {
+    return 8 * (((r * KC * 128 + 1023) / 1024) + r * KC) * 1024 + KC * 4096 <= 160 * 1024;
+  });
+  return dispatch_rows<kRmax>(n, [&](auto rc, auto wc) {
+    return launch_nvfp4_rows_r<KC, decltype(rc)::value, decltype(wc)::value>(w, x, y, n, k, s);
+  });
 }
 
 #ifndef QGEMV_NVFP4_IMPL
-#define QGEMV_NVFP4_IMPL 2  // 1: K-split kernel only, 2: row-streaming where instantiated
+#define QGEMV_NVFP4_IMPL 2  // 1: K-split kernel only, 2: row-streaming for K <= 16384
 #endif
 
 hipError_t launch_nvfp4_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                              hipStream_t s) {
-  if (QGEMV_NVFP4_IMPL == 2 && k % 2048 == 0) {
-    if (k == 14336) return launch_nvfp4_rows<7, 2>(w, x, y, n, s);
-    if (k == 4096) return launch_nvfp4_rows<2, 8>(w, x, y, n, s);
+  if (QGEMV_NVFP4_IMPL == 2) {
+    switch ((k + 2047) / 2048) {
+      case 1: return launch_nvfp4_rows<1>(w, x, y, n, k, s);
+      case 2: return launch_nvfp4_rows<2>(w, x, y, n, k, s);
+      case 3: return launch_nvfp4_rows<3>(w, x, y, n, k, s);
+      case 4: return launch_nvfp4_rows<4>(w, x, y, n, k, s);
+      case 5: return launch_nvfp4_rows<5>(w, x, y, n, k, s);
+      case 6: return launch_nvfp4_rows<6>(w, x, y, n, k, s);
+      case 7: return launch_nvfp4_rows<7>(w, x, y, n, k, s);
+      case 8: return launch_nvfp4_rows<8>(w, x, y, n, k, s);
+      default: break;
+    }
   }
   return launch_nvfp4_r<QGEMV_NVFP4_R>(w, x, y, n, k, s);
 }

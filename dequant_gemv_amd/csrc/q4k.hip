@@ -396,37 +396,35 @@ static hipError_t launch_q4k_rows_r(const void* w, const void* x, float* y, int6
   return hipGetLastError();
 }
 
-// Shape -> (R rows per wave, W waves per workgroup).  Up to 1024 rows: one
-// row per wave, 4 waves per workgroup (up to one wave per SIMD).  Beyond: 8
-// waves (two per SIMD, so one wave's LDS latency hides behind the other's
-// arithmetic) and R = ceil(N / 2048), i.e. about 256 workgroups that all run
-// at once; for N past what fits, a smaller stage so two workgroups share a CU
-// and one's loads overlap the other's tail.
-static bool launch_q4k_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s,
-                            hipError_t* err) {
-  const int nb = (int)(k / 256);
-  const int kc = (nb + 7) / 8;
-  const int64_t r8 = (n + 2047) / 2048;
-  if (kc == 7) {
-    if (n <= 1024) *err = launch_q4k_rows_r<7, 1, 4>(w, x, y, n, k, s);
-    else if (r8 <= 1) *err = launch_q4k_rows_r<7, 1, 8>(w, x, y, n, k, s);
-    else *err = launch_q4k_rows_r<7, 2, 8>(w, x, y, n, k, s);
-    return true;
-  }
-  if (kc == 2) {
-    if (n <= 1024) *err = launch_q4k_rows_r<2, 1, 4>(w, x, y, n, k, s);
-    else if (r8 <= 1) *err = launch_q4k_rows_r<2, 1, 8>(w, x, y, n, k, s);
-    else if (r8 <= 2) *err = launch_q4k_rows_r<2, 2, 8>(w, x, y, n, k, s);
-    else if (r8 <= 4) *err = launch_q4k_rows_r<2, 4, 8>(w, x, y, n, k, s);
-    else if (r8 <= 7) *err = launch_q4k_rows_r<2, 7, 8>(w, x, y, n, k, s);
-    else if (r8 <= 8) *err = launch_q4k_rows_r<2, 8, 8>(w, x, y, n, k, s);
-    else *err = launch_q4k_rows_r<2, 4, 8>(w, x, y, n, k, s);
-    return true;
-  }
-  return false;
+template <int KC>
+static hipError_t launch_q4k_rows_kc(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+  constexpr int kRmax = largest_fitting_r([](int r) {
+    return 8 * ((r * KC * 8 * kQ4kBytes + 1023) / 1024) * 1024 + KC * 4096 <= 160 * 1024;
+  });
+  return dispatch_rows<kRmax>(n, [&](auto rc, auto wc) {
+    return launch_q4k_rows_r<KC, decltype(rc)::value, decltype(wc)::value>(w, x, y, n, k, s);
+  });
 }
 
-// 1: K-split kernel only, 2: row-streaming kernel where instantiated (K-split otherwise)
+// Row streaming for K up to 16384 (at most 8 K-chunks of 2048); false when K
+// is larger (the K-split kernel takes it).
+static bool launch_q4k_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s,
+                            hipError_t* err) {
+  const int kc = (int)((k / 256 + 7) / 8);
+  switch (kc) {
+    case 1: *err = launch_q4k_rows_kc<1>(w, x, y, n, k, s); return true;
+    case 2: *err = launch_q4k_rows_kc<2>(w, x, y, n, k, s); return true;
+    case 3: *err = launch_q4k_rows_kc<3>(w, x, y, n, k, s); return true;
+    case 4: *err = launch_q4k_rows_kc<4>(w, x, y, n, k, s); return true;
+    case 5: *err = launch_q4k_rows_kc<5>(w, x, y, n, k, s); return true;
+    case 6: *err = launch_q4k_rows_kc<6>(w, x, y, n, k, s); return true;
+    case 7: *err = launch_q4k_rows_kc<7>(w, x, y, n, k, s); return true;
+    case 8: *err = launch_q4k_rows_kc<8>(w, x, y, n, k, s); return true;
+    default: return false;
+  }
+}
+
+// 1: K-split kernel only, 2: row-streaming kernel for K <= 16384 (K-split beyond)
 #ifndef QGEMV_Q4K_IMPL
 #define QGEMV_Q4K_IMPL 2
 #endif

@@ -75,4 +75,42 @@ __device__ __forceinline__ void store_rows(float (&acc)[R], float* __restrict__ 
   if (lane >= 48 && j < nrows) y[row0 + j] = t * scale;
 }
 
+// Shape -> (R rows per wave, W waves per workgroup) of a row-streaming
+// kernel: up to 1024 rows one row per wave and 4 waves per workgroup (up to
+// one wave per SIMD); beyond, 8 waves (two per SIMD, so one wave's LDS
+// latency hides behind the other's arithmetic) and R = ceil(N / 2048), i.e.
+// about 256 workgroups that all run at once; past what RMAX (the largest R
+// whose stage fits LDS at 8 waves) allows, R = min(4, RMAX) so that two
+// workgroups can share a CU and one's loads overlap the other's tail.
+// `launch(Int<R>{}, Int<W>{})` launches the instantiation.
+template <int RMAX, typename Launch>
+hipError_t dispatch_rows(int64_t n, Launch&& launch) {
+  static_assert(RMAX >= 1, "no configuration fits");
+  if (n <= 1024) return launch(Int<1>{}, Int<4>{});
+  const int64_t r8 = (n + 2047) / 2048;
+  if (RMAX < 2 || r8 <= 1) return launch(Int<1>{}, Int<8>{});
+  if constexpr (RMAX >= 2) {
+    if (RMAX < 4 || r8 <= 2) return launch(Int<2>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 4) {
+    if (RMAX < 7 || r8 <= 4) return launch(Int<4>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 7) {
+    if (r8 <= 7) return launch(Int<7>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 8) {
+    if (r8 <= 8) return launch(Int<8>{}, Int<8>{});
+  }
+  return launch(Int<(RMAX >= 4 ? 4 : RMAX >= 2 ? 2 : 1)>{}, Int<8>{});
+}
+
+// Largest R <= 16 for which FITS(R) holds (FITS: a constexpr predicate).
+template <typename Fits>
+constexpr int largest_fitting_r(Fits fits) {
+  int best = 0;
+  for (int r = 1; r <= 16; ++r)
+    if (fits(r)) best = r;
+  return best;
+}
+
 }  // namespace qgemv

@@ -193,9 +193,11 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void tq1_gemv_kernel(const uin
 }
 
 
-// Row-streaming variant (K a multiple of 4096): a wave owns R whole rows,
-// whose bytes are one contiguous run of R*KS segments of 864 bytes (16 blocks)
-// streamed into the wave's LDS stage with the shared lookahead schedule.
+// Row-streaming variant (K a multiple of 2048, up to 8192): a wave owns R
+// whole rows, whose bytes are one contiguous run of R*KS segments of up to
+// 864 bytes (16 blocks; the last segment of a row may hold 8) streamed into
+// the wave's LDS stage with the shared lookahead schedule (a row of 8m blocks
+// is 432m bytes, so every segment starts 16-byte aligned).
 // Lane l < 54 takes bytes 16l..16l+15 of every segment, as in the K-split
 // kernel; its 8 x 5 activation pairs and per-block-slot sums are read once
 // per segment position from the workgroup's LDS copy of x and reused for all
@@ -220,10 +222,11 @@ struct Tq1Rows {
 template <int KS, int R, int W>
 __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __restrict__ w,
                                                               const uint16_t* __restrict__ x,
-                                                              float* __restrict__ y, int n) {
+                                                              float* __restrict__ y, int n, int nb) {
   using C = Tq1Rows<KS, R, W>;
-  using S = typename C::S;
-  constexpr int kRowBytes = KS * kTq1SegBytes;
+  using S = typename C::S;  // assumes full segments; a short last segment only ends earlier
+  const int kRowBytes = nb * kTq1Bytes;
+  const int nbs_last = nb - (KS - 1) * kTq1SegBlocks;  // 8 or 16
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
   unsigned char* const xs = lds + W * S::kStage;
   const int lane = __lane_id();
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   const int row0 = (blockIdx.x * W + wave) * R;
   const int nrows = max(0, min(R, n - row0));
 
-  load_shared_pieces<8 * KS, W>(make_rsrc(x, (uint32_t)KS * 8192u), xs, wave, lane,
+  load_shared_pieces<8 * KS, W>(make_rsrc(x, (uint32_t)nb * 512u), xs, wave, lane,
                                 [](int piece, int i) { return (uint32_t)(piece * 1024 + 16 * i); });
   const auto wr = make_rsrc(w + (int64_t)row0 * kRowBytes, (uint32_t)(nrows * kRowBytes));
   stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX>(wr, stage, lane);
@@ -246,8 +249,11 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     if ((o0 + 2 * i) / kTq1Bytes != blk0 && bnd == 8) bnd = i;
-  const bool two = active && bnd < 8 && blk0 + 1 < kTq1SegBlocks;  // second slot is a block of the segment
-  const int dof0 = blk0 * kTq1Bytes + 52, dof1 = two ? (blk0 + 1) * kTq1Bytes + 52 : dof0;
+  // per segment: the lane's first / second block slot holds a block of the segment
+  auto slot0 = [&](int sg) { return active && blk0 < (sg == KS - 1 ? nbs_last : kTq1SegBlocks); };
+  auto slot1 = [&](int sg) { return active && bnd < 8 && blk0 + 1 < (sg == KS - 1 ? nbs_last : kTq1SegBlocks); };
+  const int dof0 = blk0 * kTq1Bytes + 52;
+  const int dof1 = (bnd < 8 && blk0 + 1 < kTq1SegBlocks) ? (blk0 + 1) * kTq1Bytes + 52 : dof0;
 
   unsigned char* const zero = xs + C::kXBytes;
   if (wave == 0 && lane == 0) {
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
       const int pos = o - blk * kTq1Bytes;
       const int base = pos < 32 ? pos : pos < 48 ? pos + 128 : pos + 192;
       const int stride = pos < 32 ? 64 : pos < 48 ? 32 : 8;  // bytes
-      const bool payload = active && pos < 52;
+      const bool payload = slot0(sg) && pos < 52 && (blk == blk0 || slot1(sg));
       const unsigned char* p0 = payload ? xs + sg * 8192 + (blk * 256 + base) * 2 : zero;
       const int st = payload ? stride : 0;
 #pragma unroll
@@ -299,12 +305,12 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   static_for<0, R * KS>([&](auto uc) {
     constexpr int U = decltype(uc)::value, r = U / KS, sg = U % KS;
     wait_vm<S::wait_count(U)>();
-    const unsigned char* seg = stage + U * kTq1SegBytes;
+    const unsigned char* seg = stage + r * kRowBytes + sg * kTq1SegBytes;
     const u32x4 raw = *reinterpret_cast<const u32x4*>(seg + o0);
     const unsigned short db0 = *reinterpret_cast<const unsigned short*>(seg + dof0);
     const unsigned short db1 = *reinterpret_cast<const unsigned short*>(seg + dof1);
-    const float d0 = active ? (float)__builtin_bit_cast(_Float16, db0) : 0.f;
-    const float d1 = two ? (float)__builtin_bit_cast(_Float16, db1) : 0.f;
+    const float d0 = slot0(sg) ? (float)__builtin_bit_cast(_Float16, db0) : 0.f;
+    const float d1 = slot1(sg) ? (float)__builtin_bit_cast(_Float16, db1) : 0.f;
     const unsigned dw[4] = {raw.x, raw.y, raw.z, raw.w};
     float a = 0.f, snap = 0.f;
 #pragma unroll
@@ -371,30 +377,33 @@ static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n
 }
 
 template <int KS, int R, int W>
-static hipError_t launch_tq1_rows_r(const void* w, const void* x, float* y, int64_t n, hipStream_t s) {
+static hipError_t launch_tq1_rows_r(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
   const int64_t rows_per_wg = (int64_t)W * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL((tq1_gemv_rows_kernel<KS, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
-                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n);
+                     (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)(k / 256));
   return hipGetLastError();
 }
 
+template <int KS>
+static hipError_t launch_tq1_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+  constexpr int kRmax = largest_fitting_r([](int r) {
+    return 8 * ((r * KS * kTq1SegBytes + 1023) / 1024) * 1024 + KS * 8192 + 16 <= 160 * 1024;
+  });
+  return dispatch_rows<kRmax>(n, [&](auto rc, auto wc) {
+    return launch_tq1_rows_r<KS, decltype(rc)::value, decltype(wc)::value>(w, x, y, n, k, s);
+  });
+}
+
 #ifndef QGEMV_TQ1_IMPL
-#define QGEMV_TQ1_IMPL 2  // 1: K-split kernel only, 2: row-streaming where instantiated
+#define QGEMV_TQ1_IMPL 2  // 1: K-split kernel only, 2: row-streaming for K % 2048 == 0, K <= 8192
 #endif
 
-// Shape -> (R rows per wave, W waves per workgroup), as for Q4_K.
 hipError_t launch_tq1_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
                            hipStream_t s) {
-  if (QGEMV_TQ1_IMPL == 2 && k == 4096) {
-    const int64_t r8 = (n + 2047) / 2048;
-    if (n <= 1024) return launch_tq1_rows_r<1, 1, 4>(w, x, y, n, s);
-    if (r8 <= 1) return launch_tq1_rows_r<1, 1, 8>(w, x, y, n, s);
-    if (r8 <= 2) return launch_tq1_rows_r<1, 2, 8>(w, x, y, n, s);
-    if (r8 <= 4) return launch_tq1_rows_r<1, 4, 8>(w, x, y, n, s);
-    if (r8 <= 7) return launch_tq1_rows_r<1, 7, 8>(w, x, y, n, s);
-    if (r8 <= 8) return launch_tq1_rows_r<1, 8, 8>(w, x, y, n, s);
-    return launch_tq1_rows_r<1, 8, 8>(w, x, y, n, s);
+  if (QGEMV_TQ1_IMPL == 2 && k % 2048 == 0) {
+    if (k <= 4096) return launch_tq1_rows<1>(w, x, y, n, k, s);
+    if (k <= 8192) return launch_tq1_rows<2>(w, x, y, n, k, s);
   }
   return launch_tq1_r<QGEMV_TQ1_R>(w, x, y, n, k, s);
 }

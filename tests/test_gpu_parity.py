@@ -146,7 +146,16 @@ def test_gemv_small(q, fmt, n, k):
 # kernels (the shape decides it), with ragged last workgroups.
 ROW_STREAM = [(fmt, n, k) for fmt in ("nvfp4", "tq1") for n, k in (
     (1500, 4096), (3000, 4096), (5000, 4096), (14336, 4096), (16000, 4096))] + [
-    ("nvfp4", 1500, 14336), ("nvfp4", 5000, 14336)]
+    ("nvfp4", 1500, 14336), ("nvfp4", 5000, 14336)] + [
+    # every K-chunk count up to 8 (K <= 16384), ragged last chunks, and N past
+    # one round of workgroups
+    ("q4k", 2500, 256), ("q4k", 700, 1280), ("q4k", 20000, 2048), ("q4k", 3000, 5120),
+    ("q4k", 1100, 8192), ("q4k", 300, 11008), ("q4k", 2100, 12288), ("q4k", 1500, 16384),
+    ("q4k", 5000, 16384), ("q4k", 4500, 10240),
+    ("nvfp4", 2100, 96), ("nvfp4", 1100, 1056), ("nvfp4", 3000, 5120), ("nvfp4", 5000, 12288),
+    ("nvfp4", 700, 16384), ("nvfp4", 2200, 10272), ("nvfp4", 1500, 6176),
+    ("tq1", 700, 2048), ("tq1", 2100, 2048), ("tq1", 3000, 6144), ("tq1", 5000, 8192),
+]
 
 
 @pytest.mark.parametrize("fmt,n,k", ROW_STREAM)
