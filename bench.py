@@ -172,6 +172,90 @@ def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
     return res
 
 
+# Llama-8B per-token decode: per layer Q, K, V, O (attention), gate, up, down
+# (MLP), 32 layers, then lm_head: 225 batch-1 GEMVs (rows, K).
+LLAMA8B_LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
+                 ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
+LLAMA8B_HEAD = ("lm_head", 128256, 4096)
+SWEEP_MIXES = {
+    # attention and lm_head Q4_K, gate/up TQ1_0, down NVFP4
+    "mixed": {"q": "q4k", "k": "q4k", "v": "q4k", "o": "q4k", "gate": "tq1", "up": "tq1",
+              "down": "nvfp4", "lm_head": "q4k"},
+    "q4k": None, "nvfp4": None, "tq1": None,  # every matrix in one format
+}
+
+
+def measure_sweep(mix: str, tokens: int, layers: int = 32):
+    """One token = the 225 GEMVs of a Llama-8B decode step, each layer with its
+    own weight buffers (cloned on the device from one generated matrix per
+    shape, so every launch reads cold bytes: ~2.9 GB for the mixed sweep),
+    captured in one HIP graph and replayed per token."""
+    import numpy as np
+    import torch
+
+    from dequant_gemv_amd import qgemv, synth
+
+    dev = torch.device("cuda:0")
+    fmt_of = SWEEP_MIXES[mix] or {r: mix for r, _, _ in LLAMA8B_LAYER + [LLAMA8B_HEAD]}
+    proto, xs = {}, {}
+    for role, n, k in LLAMA8B_LAYER + [LLAMA8B_HEAD]:
+        fmt = fmt_of[role]
+        key = (fmt, n, k)
+        if key not in proto:
+            seed = 3000 + len(proto)
+            proto[key] = torch.from_numpy(synth.weights(fmt, n, k, seed)).to(dev)
+            xs[key] = torch.from_numpy(synth.activations(fmt, k, seed + 1).view(np.int16).copy()).to(dev)
+    calls, total_bytes = [], 0
+    for layer in range(layers):
+        for role, n, k in LLAMA8B_LAYER:
+            fmt = fmt_of[role]
+            w = proto[(fmt, n, k)].clone()
+            calls.append((fmt, w, xs[(fmt, n, k)], torch.empty(n, dtype=torch.float32, device=dev), n, k))
+            total_bytes += algorithmic_bytes(fmt, n, k)
+    role, n, k = LLAMA8B_HEAD
+    fmt = fmt_of[role]
+    calls.append((fmt, proto[(fmt, n, k)], xs[(fmt, n, k)], torch.empty(n, dtype=torch.float32, device=dev), n, k))
+    total_bytes += algorithmic_bytes(fmt, n, k)
+    stream = torch.cuda.Stream()
+    h = stream.cuda_stream
+
+    def token():
+        for fmt, w, x, y, n, k in calls:
+            qgemv.GEMV[fmt](w, x, y, n, k, h)
+
+    with torch.cuda.stream(stream):
+        token()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        token()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(tokens):
+            g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * ev0.elapsed_time(ev1) / tokens
+    res = {
+        "workload": f"Llama-8B decode step, {len(calls)} GEMVs ({layers} layers + lm_head), formats: {mix}",
+        "gemvs_per_token": len(calls),
+        "algorithmic_bytes_per_token": total_bytes,
+        "us_per_token": round(us, 2),
+        "gbps": round(total_bytes / (us * 1e-6) / 1e9, 1),
+        "pct_of_hbm_peak": round(100 * total_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+        "tokens_timed": tokens,
+    }
+    del calls, proto, xs, g
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(fmt, n, k, budget_s=10.0):
     """The fp64 oracle as it stands, all host cores, on the same workload."""
     import numpy as np
@@ -215,6 +299,9 @@ def main():
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-extra", action="store_true", help="skip the other formats' shapes")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sweep", default="mixed",
+                    help="Llama-8B per-token sweep(s) to time among mixed,q4k,nvfp4,tq1 (comma list; 'none' to skip)")
+    ap.add_argument("--sweep-tokens", type=int, default=20)
     ap.add_argument("--fmt", default=None, help="measure only this format (q4k, nvfp4, tq1) at N,K")
     ap.add_argument("--n", type=int, default=None)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -267,6 +354,13 @@ def main():
             }
             log(f"[bench] {efmt} {en}x{ek}: {r['us_per_launch_event']:.3f} us, {r['gbps_event']:.1f} GB/s")
 
+    sweeps = {}
+    if not args.no_extra and not args.fmt and args.sweep != "none":
+        for mix in args.sweep.split(","):
+            r = measure_sweep(mix, args.sweep_tokens)
+            sweeps[mix] = r
+            log(f"[bench] sweep {mix}: {r['us_per_token']} us/token, {r['gbps']} GB/s over {r['gemvs_per_token']} GEMVs")
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(fmt, n, k)
@@ -308,6 +402,7 @@ def main():
                          "note": "pure dwordx4 read of the same weight bytes, same rotation"},
         "cpu_baseline": cpu,
         "other_shapes": extra,
+        "decode_sweep": sweeps,
         "build_id": have,
         "gpu": torch.cuda.get_device_name(0),
     }

@@ -185,6 +185,9 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
   static_for<0, R * KC>([&](auto uc) {
     constexpr int U = decltype(uc)::value, r = U / KC, ch = U % KC;
     wait_vm<S::wait_count(U)>();
+    // refill first: the stage holds the whole run (no unread byte is
+    // overwritten) and the arithmetic stays off the load path
+    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
     const u32x4 nv = *reinterpret_cast<const u32x4*>(nib_stage + r * kNibRow + ch * 1024 + 16 * lane);
     const unsigned sc = *reinterpret_cast<const uint16_t*>(sc_stage + r * kScRow + ch * 128 + 2 * lane);
     const unsigned q[4] = {nv.x, nv.y, nv.z, nv.w};
@@ -201,8 +204,6 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
       s1 = tail_ok ? s1 : 0.f;
     }
     acc[r] = __builtin_fmaf(s1, a1, __builtin_fmaf(s0, a0, acc[r]));
-    // refill: this unit's LDS reads have completed (their data was used above)
-    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
   });
   store_rows<R>(acc, y, row0, nrows, 1.f, lane);
 }

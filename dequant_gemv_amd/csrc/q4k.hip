@@ -219,7 +219,7 @@ __device__ __forceinline__ constexpr int q4k_xswz(int g) {
 }
 
 #ifndef QGEMV_Q4K_AHEAD
-#define QGEMV_Q4K_AHEAD 4  // weight loads in flight per wave beyond the unit being consumed
+#define QGEMV_Q4K_AHEAD 3  // weight loads in flight per wave beyond the unit being consumed
 #endif
 
 template <int KC, int R, int W>
@@ -306,6 +306,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
   static_for<0, R * KC>([&](auto u) {
     constexpr int U = decltype(u)::value, r = U / KC, ch = U % KC;
     wait_vm<S::wait_count(U)>();
+    // refill first: the stage holds the whole run, so the next loads never
+    // overwrite unread bytes, and issuing them before this unit's arithmetic
+    // keeps the arithmetic off the load path
+    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(wr, stage, lane);
     const unsigned char* blk = stage + r * row_bytes + ch * C::kUnitBytes + bl * kQ4kBytes;
     const u32x4 hdr = *reinterpret_cast<const u32x4*>(blk);
     const u32x4 qv = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * p);
@@ -331,8 +335,6 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
       acc[r] += tail_ok ? part : 0.f;
     else
       acc[r] += part;
-    // refill: this unit's LDS reads have completed (their data was used above)
-    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(wr, stage, lane);
   });
   store_rows<R>(acc, y, row0, nrows, 0x1p24f, lane);
 }

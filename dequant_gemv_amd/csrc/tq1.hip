@@ -305,6 +305,9 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   static_for<0, R * KS>([&](auto uc) {
     constexpr int U = decltype(uc)::value, r = U / KS, sg = U % KS;
     wait_vm<S::wait_count(U)>();
+    // refill first: the stage holds the whole run (no unread byte is
+    // overwritten) and the arithmetic stays off the load path
+    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(wr, stage, lane);
     const unsigned char* seg = stage + r * kRowBytes + sg * kTq1SegBytes;
     const u32x4 raw = *reinterpret_cast<const u32x4*>(seg + o0);
     const unsigned short db0 = *reinterpret_cast<const unsigned short*>(seg + dof0);
@@ -324,8 +327,6 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
     }
     const float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0[sg]), acc[r]);
     acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1[sg]), t);
-    // refill: this unit's LDS reads have completed (their data was used above)
-    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(wr, stage, lane);
   });
   store_rows<R>(acc, y, row0, nrows, 1.f, lane);
 }
