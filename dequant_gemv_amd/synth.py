@@ -21,7 +21,11 @@ Distributions follow the Llama-8B-shaped decode workloads the pages measure:
   each qh byte uniformly from the 81 four-trit codes (fifth trit zero).
   ``d`` ~ U(1e-2, 5e-2) in fp16.
 
-Activations are fp16 (Q4_K, TQ1_0) or bf16 (NVFP4) draws of N(0, 1).
+* Dense fp16 / bf16 (the Mojo page's bf16 comparison GEMV): weights
+  N(0, 0.02) rounded to nearest-even in the element type, [n][k] row-major.
+
+Activations are fp16 (Q4_K, TQ1_0, dense fp16) or bf16 (NVFP4, dense bf16)
+draws of N(0, 1); the epilogue's c vector is N(0, 1) in its element type.
 
 All draws use numpy's PCG64 so a seed names one input exactly.
 """
@@ -106,12 +110,40 @@ def tq1_weights(n: int, k: int, seed: int) -> np.ndarray:
     return blk.reshape(n, nb * TQ1_BLOCK_BYTES)
 
 
+def f16_weights(n: int, k: int, seed: int, sigma: float = 0.02) -> np.ndarray:
+    """Dense fp16 matrix [n][k] as n*k*2 little-endian bytes."""
+    v = (_rng(seed).standard_normal((n, k)) * sigma).astype(np.float16)
+    return v.view(np.uint8).reshape(n, 2 * k)
+
+
+def bf16_weights(n: int, k: int, seed: int, sigma: float = 0.02) -> np.ndarray:
+    """Dense bf16 matrix [n][k] as n*k*2 little-endian bytes."""
+    import torch
+
+    v = torch.from_numpy((_rng(seed).standard_normal((n, k)) * sigma).astype(np.float32))
+    bits = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return bits.view(np.uint8).reshape(n, 2 * k).copy()
+
+
 def weights(fmt: str, n: int, k: int, seed: int) -> np.ndarray:
-    return {"q4k": q4k_weights, "nvfp4": nvfp4_weights, "tq1": tq1_weights}[fmt](n, k, seed)
+    return {"q4k": q4k_weights, "nvfp4": nvfp4_weights, "tq1": tq1_weights,
+            "f16": f16_weights, "bf16": bf16_weights}[fmt](n, k, seed)
+
+
+def x_dtype(fmt: str) -> str:
+    """Element type of the activations of a weight format."""
+    return "bf16" if fmt in ("nvfp4", "bf16") else "f16"
 
 
 def activations(fmt: str, k: int, seed: int) -> np.ndarray:
-    return x_bf16(k, seed) if fmt == "nvfp4" else x_f16(k, seed)
+    return x_bf16(k, seed) if x_dtype(fmt) == "bf16" else x_f16(k, seed)
+
+
+def vector(n: int, dtype: str, seed: int) -> np.ndarray:
+    """N(0, 1) vector of n elements: float32 for "f32", else fp16 / bf16 codes."""
+    if dtype == "f32":
+        return _rng(seed).standard_normal(n).astype(np.float32)
+    return x_bf16(n, seed) if dtype == "bf16" else x_f16(n, seed)
 
 
 def weight_bytes(fmt: str, n: int, k: int) -> int:
@@ -122,4 +154,6 @@ def weight_bytes(fmt: str, n: int, k: int) -> int:
         return n * (k // QK) * TQ1_BLOCK_BYTES
     if fmt == "nvfp4":
         return n * k // 2 + n * k // NVFP4_SF
+    if fmt in ("f16", "bf16"):
+        return 2 * n * k
     raise ValueError(fmt)

@@ -15,7 +15,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FMT = {"q4k": 0, "nvfp4": 1, "tq1": 2}
+FMT = {"q4k": 0, "nvfp4": 1, "tq1": 2, "f16": 3, "bf16": 4}
+# element types of materialised rows, epilogue inputs and outputs
+DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
 
 _lib = None
 
@@ -46,6 +48,12 @@ def _load():
     lib.oracle_e4m3.argtypes = [ctypes.c_uint8]
     lib.oracle_e2m1.restype = ctypes.c_double
     lib.oracle_e2m1.argtypes = [ctypes.c_uint8]
+    lib.oracle_round_f16.restype = ctypes.c_uint16
+    lib.oracle_round_f16.argtypes = [ctypes.c_double]
+    lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_get_rows.argtypes = [ctypes.c_int, P, I64, I64, P, I64, ctypes.c_int, P]
+    lib.oracle_decode16.argtypes = [ctypes.c_int, P, I64, P]
     lib.oracle_tq1_digit.restype = ctypes.c_int
     lib.oracle_tq1_digit.argtypes = [ctypes.c_uint8, ctypes.c_int]
     lib.oracle_threads.restype = ctypes.c_int
@@ -76,6 +84,25 @@ def e2m1(n: int) -> float:
     return _load().oracle_e2m1(n)
 
 
+def round_f16(v: float) -> int:
+    """Bits of the binary16 nearest to ``v`` (ties to even)."""
+    return _load().oracle_round_f16(float(v))
+
+
+def round_bf16(v: float) -> int:
+    """Bits of the bfloat16 nearest to ``v`` (ties to even)."""
+    return _load().oracle_round_bf16(float(v))
+
+
+def decode16(dtype: str, h: np.ndarray) -> np.ndarray:
+    """fp64 values of 16-bit codes of ``dtype`` ("f16" or "bf16")."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.size, dtype=np.float64)
+    if h.size:
+        _load().oracle_decode16(DTYPE[dtype], _ptr(h), h.size, _ptr(out))
+    return out.reshape(h.shape)
+
+
 def tq1_digit(b: int, k: int) -> int:
     return _load().oracle_tq1_digit(b, k)
 
@@ -93,6 +120,19 @@ def dequant(fmt: str, w: np.ndarray, n: int, k: int) -> np.ndarray:
     w = np.ascontiguousarray(w, dtype=np.uint8)
     out = np.empty((n, k), dtype=np.float64)
     _load().oracle_dequant(FMT[fmt], _ptr(w), n, k, _ptr(out))
+    return out
+
+
+def get_rows(fmt: str, w: np.ndarray, n: int, k: int, rows, out_dtype: str) -> np.ndarray:
+    """Rows ``rows`` of the weights as [len(rows), k] codes of ``out_dtype``
+    (uint32 fp32 bits, or uint16 fp16 / bf16 bits): each weight rounded to
+    fp32, then to the output type; an index outside [0, n) gives quiet NaNs."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, k), dtype=np.uint32 if out_dtype == "f32" else np.uint16)
+    if rows.size:
+        _load().oracle_get_rows(FMT[fmt], _ptr(w), n, k, _ptr(rows), rows.size, DTYPE[out_dtype],
+                                _ptr(out))
     return out
 
 
@@ -115,3 +155,30 @@ def gemv(fmt: str, w: np.ndarray, x: np.ndarray, n: int, k: int, rows=None):
     if cnt:
         _load().oracle_gemv(FMT[fmt], _ptr(w), _ptr(x), n, k, rp, cnt, _ptr(y), _ptr(a))
     return y, a
+
+
+def c_values(c: np.ndarray, c_dtype: str) -> np.ndarray:
+    """fp64 values of an epilogue input given as fp32 (float32 array) or as
+    fp16 / bf16 codes (uint16 array)."""
+    if c_dtype == "f32":
+        return np.asarray(c, dtype=np.float32).astype(np.float64)
+    return decode16(c_dtype, c)
+
+
+def gemv_ex(fmt: str, w, x, n: int, k: int, alpha: float, beta: float, c=None, c_dtype="f32",
+            rows=None):
+    """General form of the GEMV ("Writing a high performant GEMV + dequant for
+    Metal", section "What is a GEMV"): v = alpha * (x . dequant(w)^T) + beta * c
+    in fp64, with c not read when beta == 0.  Returns (v, bound) where bound =
+    |alpha| * sum_i |x_i w_ri| + |beta * c_r| scales the tolerance.  ``c`` is
+    indexed like the output (rows of ``rows`` when given)."""
+    y, a = gemv(fmt, w, x, n, k, rows=rows)
+    v = float(alpha) * y
+    bound = abs(float(alpha)) * a
+    if beta != 0.0:
+        cv = c_values(c, c_dtype)
+        if rows is not None:
+            cv = cv[np.asarray(rows, dtype=np.int64)]
+        v = v + float(beta) * cv
+        bound = bound + np.abs(float(beta) * cv)
+    return v, bound

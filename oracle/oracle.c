@@ -23,6 +23,11 @@
  *  [TQ1]  "metal: TQ1_0 kernel performance": sections 1 (qs[48] then qh[4],
  *         five digits per qs byte, four per qh byte), 2 (which elements each
  *         digit feeds) and "Not applicable" (digits from floor(3^k b / 256)).
+ *  [DENSE] The Mojo "fp4_gemv" page compares against a dense bf16 GEMV of the
+ *         same shape: w_i is the fp16 / bf16 value itself.
+ *  [ROWS] Materialising rows (the TQ1_0 page's dequantize template, the Mojo
+ *         page's fp32 dequant): out = the fp32 weight, optionally cast to
+ *         fp16 / bf16 with round-to-nearest-even.
  *
  * Readings where the pages leave a choice (all recorded in the design notes):
  *  - fp16 d at byte 0, dmin at byte 2, little-endian (Q4_K).
@@ -31,9 +36,14 @@
  *    subnormals, S.1111.111 = NaN, no infinities); the scale's sign is ignored.
  *  - TQ1_0 block = qs[48] | qh[4] | fp16 d; trit t maps to weight d*(t-1);
  *    qh digit k of byte m feeds element 240 + 4k + m.
+ *  - A 16-bit materialisation rounds the fp32 weight (not the exact one):
+ *    fp16(fp32(w)).  Only Q4_K weights can differ between the two readings.
+ *  - A row index outside [0, n) materialises as a row of the output type's
+ *    quiet NaN with a clear sign bit.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -91,6 +101,49 @@ int oracle_tq1_digit(uint8_t b, int k) {
   return (3 * r) / 256;
 }
 
+/* Nearest value of a binary floating-point format with P significand bits
+ * (implicit bit included), exponent bias BIAS and EBITS exponent bits, ties to
+ * even; returns its bit pattern (sign in bit EBITS + P - 1).  Overflow gives
+ * infinity, NaN a quiet NaN of the same sign. */
+static uint32_t round_bits(double v, int p, int bias, int ebits) {
+  const uint32_t sign = signbit(v) ? 1u << (ebits + p - 1) : 0u;
+  const uint32_t emask = (1u << ebits) - 1u;
+  const uint32_t inf = sign | (emask << (p - 1));
+  if (isnan(v))
+    return inf | (1u << (p - 2));
+  double a = fabs(v);
+  if (isinf(a))
+    return inf;
+  if (a == 0.0)
+    return sign;
+  int x;
+  frexp(a, &x);              /* a = f * 2^x, 0.5 <= f < 1 */
+  int e = x - 1;             /* 2^e <= a < 2^(e+1) */
+  const int emin = 1 - bias; /* smallest normal exponent */
+  if (e < emin)
+    e = emin; /* subnormal range: same quantum as the smallest normals */
+  int qe = e - (p - 1);      /* value of one unit in the last place */
+  double scaled = ldexp(a, -qe); /* exact: a power-of-two scaling */
+  double n = floor(scaled);
+  double frac = scaled - n;
+  if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0))
+    n += 1.0;
+  if (n == ldexp(1.0, p)) { /* rounded up to the next binade */
+    n = ldexp(1.0, p - 1);
+    qe += 1;
+  }
+  const double half = ldexp(1.0, p - 1);
+  if (n < half) /* subnormal (or zero): exponent field 0 */
+    return sign | (uint32_t)n;
+  const int field = qe + (p - 1) + bias;
+  if (field >= (int)emask)
+    return inf;
+  return sign | ((uint32_t)field << (p - 1)) | (uint32_t)(n - half);
+}
+
+uint16_t oracle_round_f16(double v) { return (uint16_t)round_bits(v, 11, 15, 5); }
+uint16_t oracle_round_bf16(double v) { return (uint16_t)round_bits(v, 8, 127, 8); }
+
 /* ---- per-block dequantisation (fp64, 256 weights) ------------------------- */
 
 static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
@@ -144,6 +197,31 @@ static double nvfp4_weight(const uint8_t* buf, int64_t n, int64_t k, int64_t r, 
   return oracle_e2m1(nib) * fabs(oracle_e4m3(sc));
 }
 
+/* Dense 16-bit weight (row r, column i): fmt 3 = fp16, 4 = bf16. */
+static double dense_weight(int fmt, const uint8_t* buf, int64_t k, int64_t r, int64_t i) {
+  uint16_t h = rd16(buf + 2 * (r * k + i));
+  return fmt == 3 ? oracle_f16(h) : oracle_bf16(h);
+}
+
+/* fp64 weights of row r, all K of them. */
+static void dequant_row(int fmt, const uint8_t* w, int64_t n, int64_t k, int64_t r, double* out) {
+  int64_t nb = k / 256;
+  if (fmt == 1) {
+    for (int64_t i = 0; i < k; ++i)
+      out[i] = nvfp4_weight(w, n, k, r, i);
+  } else if (fmt == 3 || fmt == 4) {
+    for (int64_t i = 0; i < k; ++i)
+      out[i] = dense_weight(fmt, w, k, r, i);
+  } else {
+    for (int64_t b = 0; b < nb; ++b) {
+      if (fmt == 0)
+        q4k_block(w + (r * nb + b) * 144, out + b * 256);
+      else
+        tq1_block(w + (r * nb + b) * 54, out + b * 256);
+    }
+  }
+}
+
 /* ---- public entry points --------------------------------------------------- */
 
 int oracle_threads(void) {
@@ -163,57 +241,73 @@ void oracle_set_threads(int t) {
 #endif
 }
 
-/* Dequantise rows [0, n) into out[n][k] (fp64). fmt: 0 = Q4_K, 1 = NVFP4, 2 = TQ1_0. */
+/* Dequantise rows [0, n) into out[n][k] (fp64).  fmt: 0 = Q4_K, 1 = NVFP4,
+ * 2 = TQ1_0, 3 = dense fp16, 4 = dense bf16. */
 void oracle_dequant(int fmt, const uint8_t* w, int64_t n, int64_t k, double* out) {
-  int64_t nb = k / 256;
 #pragma omp parallel for schedule(static)
-  for (int64_t r = 0; r < n; ++r) {
-    if (fmt == 1) {
-      for (int64_t i = 0; i < k; ++i)
-        out[r * k + i] = nvfp4_weight(w, n, k, r, i);
-    } else {
-      for (int64_t b = 0; b < nb; ++b) {
-        if (fmt == 0)
-          q4k_block(w + (r * nb + b) * 144, out + r * k + b * 256);
+  for (int64_t r = 0; r < n; ++r)
+    dequant_row(fmt, w, n, k, r, out + r * k);
+}
+
+/* Rows rows[0..nrows) of the weights, each weight rounded to fp32 and then to
+ * the output type (0 = fp32, 1 = fp16, 2 = bf16), into out[nrows][k] (4- or
+ * 2-byte elements).  An index outside [0, n) gives a row of quiet NaNs. */
+void oracle_get_rows(int fmt, const uint8_t* w, int64_t n, int64_t k, const int64_t* rows,
+                     int64_t nrows, int out_dtype, void* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < nrows; ++j) {
+    int64_t r = rows[j];
+    double* row = (double*)malloc((size_t)k * sizeof(double));
+    int valid = r >= 0 && r < n;
+    if (valid)
+      dequant_row(fmt, w, n, k, r, row);
+    for (int64_t i = 0; i < k; ++i) {
+      const int64_t o = j * k + i;
+      if (!valid) {
+        if (out_dtype == 0)
+          ((uint32_t*)out)[o] = 0x7FC00000u;
         else
-          tq1_block(w + (r * nb + b) * 54, out + r * k + b * 256);
+          ((uint16_t*)out)[o] = out_dtype == 1 ? 0x7E00 : 0x7FC0;
+        continue;
       }
+      const float f = (float)row[i]; /* round to nearest even (C default mode) */
+      if (out_dtype == 0)
+        memcpy((uint32_t*)out + o, &f, sizeof f);
+      else if (out_dtype == 1)
+        ((uint16_t*)out)[o] = oracle_round_f16((double)f);
+      else
+        ((uint16_t*)out)[o] = oracle_round_bf16((double)f);
     }
+    free(row);
   }
+}
+
+/* Decode n 16-bit values (dtype 1 = fp16, 2 = bf16) to fp64. */
+void oracle_decode16(int dtype, const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = dtype == 1 ? oracle_f16(h[i]) : oracle_bf16(h[i]);
 }
 
 /* y[r] = sum_i x_i w_ri and a[r] = sum_i |x_i w_ri| over rows listed in
  * rows[0..nrows) (rows == NULL means all n rows, in order).  x holds fp16 bits
- * (Q4_K, TQ1_0) or bf16 bits (NVFP4). */
+ * (Q4_K, TQ1_0, dense fp16) or bf16 bits (NVFP4, dense bf16). */
 void oracle_gemv(int fmt, const uint8_t* w, const uint16_t* x, int64_t n, int64_t k,
                  const int64_t* rows, int64_t nrows, double* y, double* a) {
-  int64_t nb = k / 256;
   if (rows == NULL)
     nrows = n;
+  const int x_bf16 = fmt == 1 || fmt == 4;
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t t = 0; t < nrows; ++t) {
     int64_t r = rows ? rows[t] : t;
     double acc = 0.0, aacc = 0.0;
-    double wb[256];
-    if (fmt == 1) {
-      for (int64_t i = 0; i < k; ++i) {
-        double p = oracle_bf16(x[i]) * nvfp4_weight(w, n, k, r, i);
-        acc += p;
-        aacc += fabs(p);
-      }
-    } else {
-      for (int64_t b = 0; b < nb; ++b) {
-        if (fmt == 0)
-          q4k_block(w + (r * nb + b) * 144, wb);
-        else
-          tq1_block(w + (r * nb + b) * 54, wb);
-        for (int i = 0; i < 256; ++i) {
-          double p = oracle_f16(x[b * 256 + i]) * wb[i];
-          acc += p;
-          aacc += fabs(p);
-        }
-      }
+    double* wr = (double*)malloc((size_t)k * sizeof(double));
+    dequant_row(fmt, w, n, k, r, wr);
+    for (int64_t i = 0; i < k; ++i) {
+      double p = (x_bf16 ? oracle_bf16(x[i]) : oracle_f16(x[i])) * wr[i];
+      acc += p;
+      aacc += fabs(p);
     }
+    free(wr);
     y[t] = acc;
     a[t] = aacc;
   }
