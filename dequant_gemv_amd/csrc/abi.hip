@@ -19,17 +19,33 @@ thread_local int g_last_hip_error = 0;
 constexpr int64_t kMaxK = int64_t(1) << 24;
 constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
 
-enum Fmt { kQ4k, kNvfp4, kTq1 };
+enum Fmt { kQ4k, kNvfp4, kTq1, kDenseF16, kDenseBF16 };
 
-int64_t k_multiple(Fmt f) { return f == kNvfp4 ? 32 : 256; }
+bool dense(Fmt f) { return f == kDenseF16 || f == kDenseBF16; }
+
+int64_t k_multiple(Fmt f) {
+  switch (f) {
+    case kNvfp4: return 32;
+    case kDenseF16:
+    case kDenseBF16: return 8;
+    default: return 256;
+  }
+}
+
+int64_t k_max(Fmt f) { return dense(f) ? qgemv::kDenseMaxK : kMaxK; }
 
 int64_t weight_bytes(Fmt f, int64_t m, int64_t k) {
   switch (f) {
     case kQ4k: return m * (k / 256) * 144;
     case kTq1: return m * (k / 256) * 54;
-    default: return m * (k / 2) + m * (k / 16);
+    case kNvfp4: return m * (k / 2) + m * (k / 16);
+    default: return 2 * m * k;
   }
 }
+
+bool valid_dtype(int32_t t) { return t == QGEMV_F32 || t == QGEMV_F16 || t == QGEMV_BF16; }
+
+int64_t dtype_size(int32_t t) { return t == QGEMV_F32 ? 4 : 2; }
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -39,9 +55,7 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 }
 
 int check_shape(Fmt f, int64_t m, int64_t k) {
-  if (m < 0 || m > kMaxM || k <= 0 || k > kMaxK || k % k_multiple(f) != 0) return QGEMV_E_SHAPE;
-  // grid of the dequant kernels: at most m*k/16 threads in blocks of 256
-  if (m > 0 && (m * (k / 16) + 255) / 256 > kMaxM) return QGEMV_E_SHAPE;
+  if (m < 0 || m > kMaxM || k <= 0 || k > k_max(f) || k % k_multiple(f) != 0) return QGEMV_E_SHAPE;
   return QGEMV_OK;
 }
 
@@ -53,6 +67,16 @@ int finish(hipError_t e) {
   return QGEMV_OK;
 }
 
+template <typename Out>
+hipError_t launch_gemv(Fmt f, const void* w, const void* x, const Out& y, int64_t m, int64_t k, hipStream_t s) {
+  switch (f) {
+    case kQ4k: return qgemv::launch_q4k_gemv(w, x, y, m, k, s);
+    case kNvfp4: return qgemv::launch_nvfp4_gemv(w, x, y, m, k, s);
+    case kTq1: return qgemv::launch_tq1_gemv(w, x, y, m, k, s);
+    default: return qgemv::launch_dense_gemv(f == kDenseBF16, w, x, y, m, k, s);
+  }
+}
+
 int gemv(Fmt f, const void* w, const void* x, float* y, int64_t m, int64_t k, hipStream_t s) {
   int rc = check_shape(f, m, k);
   if (rc != QGEMV_OK) return rc;
@@ -60,10 +84,50 @@ int gemv(Fmt f, const void* w, const void* x, float* y, int64_t m, int64_t k, hi
   if (!w || !x || !y) return QGEMV_E_NULL;
   if (misaligned(w, 16) || misaligned(x, 16) || misaligned(y, 4)) return QGEMV_E_ALIGN;
   if (overlap(y, m * 4, w, weight_bytes(f, m, k)) || overlap(y, m * 4, x, k * 2)) return QGEMV_E_ALIAS;
+  return finish(launch_gemv(f, w, x, qgemv::OutF32{y}, m, k, s));
+}
+
+int gemv_ex(Fmt f, const void* w, const void* x, void* y, int64_t m, int64_t k, const qgemv_epilogue* ep,
+            hipStream_t s) {
+  const qgemv_epilogue plain = {1.f, 0.f, nullptr, QGEMV_F32, QGEMV_F32};
+  const qgemv_epilogue e = ep ? *ep : plain;
+  int rc = check_shape(f, m, k);
+  if (rc != QGEMV_OK) return rc;
+  if (!valid_dtype(e.y_dtype) || (e.beta != 0.f && !valid_dtype(e.c_dtype))) return QGEMV_E_DTYPE;
+  if (m == 0) return QGEMV_OK;
+  const bool use_c = e.beta != 0.f;
+  if (!w || !x || !y || (use_c && !e.c)) return QGEMV_E_NULL;
+  const int64_t ysz = dtype_size(e.y_dtype);
+  if (misaligned(w, 16) || misaligned(x, 16) || misaligned(y, (uintptr_t)ysz)) return QGEMV_E_ALIGN;
+  if (use_c && misaligned(e.c, (uintptr_t)dtype_size(e.c_dtype))) return QGEMV_E_ALIGN;
+  if (overlap(y, m * ysz, w, weight_bytes(f, m, k)) || overlap(y, m * ysz, x, k * 2)) return QGEMV_E_ALIAS;
+  if (use_c && overlap(y, m * ysz, e.c, m * dtype_size(e.c_dtype)) && !(e.c == y && e.c_dtype == e.y_dtype))
+    return QGEMV_E_ALIAS;
+  const qgemv::OutEx out{y, use_c ? e.c : nullptr, e.alpha, e.beta, use_c ? (int)e.c_dtype : (int)QGEMV_F32,
+                         (int)e.y_dtype};
+  return finish(launch_gemv(f, w, x, out, m, k, s));
+}
+
+int get_rows(Fmt f, const void* w, int64_t m, int64_t k, const int32_t* rows, int64_t nrows, void* out,
+             int32_t dtype, hipStream_t s) {
+  int rc = check_shape(f, m, k);
+  if (rc != QGEMV_OK) return rc;
+  if (nrows < 0 || nrows > kMaxM || (!rows && nrows > m)) return QGEMV_E_SHAPE;
+  if (!valid_dtype(dtype)) return QGEMV_E_DTYPE;
+  if (nrows == 0) return QGEMV_OK;
+  // tasks of 32 (Q4_K, NVFP4) or 16 (TQ1_0) weights in workgroups of up to 256
+  const int64_t tasks = f == kTq1 ? k / 16 : k / 32;
+  const int64_t per_wg = tasks < 256 ? tasks : 256;
+  if (nrows * ((tasks + per_wg - 1) / per_wg) > kMaxM) return QGEMV_E_SHAPE;
+  if ((m > 0 && !w) || !out) return QGEMV_E_NULL;
+  if (misaligned(w, 16) || misaligned(out, 16) || misaligned(rows, 4)) return QGEMV_E_ALIGN;
+  const int64_t out_bytes = nrows * k * dtype_size(dtype);
+  if (overlap(out, out_bytes, w, weight_bytes(f, m, k)) || (rows && overlap(out, out_bytes, rows, nrows * 4)))
+    return QGEMV_E_ALIAS;
   switch (f) {
-    case kQ4k: return finish(qgemv::launch_q4k_gemv(w, x, y, m, k, s));
-    case kNvfp4: return finish(qgemv::launch_nvfp4_gemv(w, x, y, m, k, s));
-    default: return finish(qgemv::launch_tq1_gemv(w, x, y, m, k, s));
+    case kQ4k: return finish(qgemv::launch_q4k_get_rows(w, m, k, rows, nrows, out, dtype, s));
+    case kNvfp4: return finish(qgemv::launch_nvfp4_get_rows(w, m, k, rows, nrows, out, dtype, s));
+    default: return finish(qgemv::launch_tq1_get_rows(w, m, k, rows, nrows, out, dtype, s));
   }
 }
 
@@ -72,13 +136,7 @@ int dequant(Fmt f, const void* w, float* out, int64_t m, int64_t k, hipStream_t 
   if (rc != QGEMV_OK) return rc;
   if (m == 0) return QGEMV_OK;
   if (!w || !out) return QGEMV_E_NULL;
-  if (misaligned(w, 16) || misaligned(out, 16)) return QGEMV_E_ALIGN;
-  if (overlap(out, m * k * 4, w, weight_bytes(f, m, k))) return QGEMV_E_ALIAS;
-  switch (f) {
-    case kQ4k: return finish(qgemv::launch_q4k_dequant(w, out, m, k, s));
-    case kNvfp4: return finish(qgemv::launch_nvfp4_dequant(w, out, m, k, s));
-    default: return finish(qgemv::launch_tq1_dequant(w, out, m, k, s));
-  }
+  return get_rows(f, w, m, k, nullptr, m, out, QGEMV_F32, s);
 }
 
 }  // namespace
@@ -104,6 +162,45 @@ int qdequant_tq1(const void* w, float* out, int64_t M, int64_t K, struct ihipStr
   return dequant(kTq1, w, out, M, K, s);
 }
 
+int qgemv_q4k_ex(const void* w, const void* x, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                 struct ihipStream_t* s) {
+  return gemv_ex(kQ4k, w, x, y, M, K, ep, s);
+}
+int qgemv_nvfp4_ex(const void* w, const void* x, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                   struct ihipStream_t* s) {
+  return gemv_ex(kNvfp4, w, x, y, M, K, ep, s);
+}
+int qgemv_tq1_ex(const void* w, const void* x, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                 struct ihipStream_t* s) {
+  return gemv_ex(kTq1, w, x, y, M, K, ep, s);
+}
+int qgemv_f16(const void* w, const void* x, float* y, int64_t M, int64_t K, struct ihipStream_t* s) {
+  return gemv(kDenseF16, w, x, y, M, K, s);
+}
+int qgemv_bf16(const void* w, const void* x, float* y, int64_t M, int64_t K, struct ihipStream_t* s) {
+  return gemv(kDenseBF16, w, x, y, M, K, s);
+}
+int qgemv_f16_ex(const void* w, const void* x, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                 struct ihipStream_t* s) {
+  return gemv_ex(kDenseF16, w, x, y, M, K, ep, s);
+}
+int qgemv_bf16_ex(const void* w, const void* x, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                  struct ihipStream_t* s) {
+  return gemv_ex(kDenseBF16, w, x, y, M, K, ep, s);
+}
+int qget_rows_q4k(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
+                  int32_t out_dtype, struct ihipStream_t* s) {
+  return get_rows(kQ4k, w, M, K, rows, nrows, out, out_dtype, s);
+}
+int qget_rows_nvfp4(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
+                    int32_t out_dtype, struct ihipStream_t* s) {
+  return get_rows(kNvfp4, w, M, K, rows, nrows, out, out_dtype, s);
+}
+int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
+                  int32_t out_dtype, struct ihipStream_t* s) {
+  return get_rows(kTq1, w, M, K, rows, nrows, out, out_dtype, s);
+}
+
 int64_t qgemv_read_sink_len(int64_t bytes) { return bytes > 0 ? qgemv::read_sink_len(bytes) : 0; }
 
 int qgemv_read_ceiling(const void* buf, int64_t bytes, float* sink, struct ihipStream_t* s) {
@@ -121,9 +218,10 @@ const char* qgemv_strerror(int code) {
     case QGEMV_OK: return "ok";
     case QGEMV_E_NULL: return "a required pointer is NULL";
     case QGEMV_E_SHAPE: return "invalid shape (M < 0, K <= 0, K not a multiple of the block, or too large)";
-    case QGEMV_E_ALIGN: return "misaligned pointer (weights and x need 16 bytes, y 4 bytes)";
+    case QGEMV_E_ALIGN: return "misaligned pointer (weights, x and rows out need 16 bytes, y and c their element size)";
     case QGEMV_E_HIP: return "the HIP runtime rejected the launch (see qgemv_last_hip_error)";
     case QGEMV_E_ALIAS: return "the output overlaps an input";
+    case QGEMV_E_DTYPE: return "unknown element type (QGEMV_F32, QGEMV_F16 or QGEMV_BF16)";
     default: return "unknown qgemv error code";
   }
 }

@@ -51,6 +51,17 @@ __device__ __forceinline__ unsigned short ld16(__amdgpu_buffer_rsrc_t r, uint32_
 
 __device__ __forceinline__ f16x2 as_h2(unsigned v) { return __builtin_bit_cast(f16x2, v); }
 
+// Pins an fp32 value in a register, so that a following conversion to a
+// 16-bit type rounds exactly this fp32 value.  Without it the compiler fuses
+// the multiply or fma that produced the value with the conversion into one
+// mixed-precision fma (v_fma_mixlo_f16): that rounds once from the exact
+// result instead of twice, and a product fused with a +0 addend turns -0
+// into +0.
+__device__ __forceinline__ float pin_f32(float v) {
+  __asm__("" : "+v"(v));
+  return v;
+}
+
 // v_dot2_f32_f16: a.x*b.x + a.y*b.y + c with fp32 accumulation.
 __device__ __forceinline__ float dot2h(unsigned a, unsigned b, float c) {
   return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);

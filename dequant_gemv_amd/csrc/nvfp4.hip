@@ -1,4 +1,4 @@
-// NVFP4 W4A16 fused dequantise + GEMV and fp32 dequantise for gfx950.
+// NVFP4 W4A16 fused dequantise + GEMV and row materialisation for gfx950.
 //
 // Format (Mojo module "fp4_gemv"): E2M1 nibbles with one FP8 E4M3 scale per 16
 // consecutive weights; weight = e2m1 * |scale|; bf16 activations, fp32
@@ -16,6 +16,7 @@
 // (algebraically equal to scaling each weight; only the rounding order moves).
 #include "device.hpp"
 #include "launch.hpp"
+#include "rows.hpp"
 #include "stream.hpp"
 
 namespace qgemv {
@@ -28,10 +29,10 @@ namespace qgemv {
 #define QGEMV_WG_WAVES 8
 #endif
 
-template <int R>
+template <int R, typename Out>
 __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void nvfp4_gemv_kernel(const uint8_t* __restrict__ w,
                                                          const uint16_t* __restrict__ x,
-                                                         float* __restrict__ y, int n, int k,
+                                                         Out out, int n, int k,
                                                          int kc, int kw, int rg) {
   __shared__ float red[16 * 16];
   const int lane = __lane_id();
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void nvfp4_gemv_kernel(const u
     float s = 0.f;
     for (int kk = 0; kk < kw; ++kk) s += red[(g * kw + kk) * R + r];
     const int row = blockIdx.x * rg * R + g * R + r;
-    if (row < n) y[row] = s;
+    if (row < n) out.put(row, s);
   }
 }
 
@@ -129,10 +130,10 @@ struct Nvfp4Rows {
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
 
-template <int KC, int R, int W>
+template <int KC, int R, int W, typename Out>
 __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* __restrict__ w,
                                                                 const uint16_t* __restrict__ x,
-                                                                float* __restrict__ y, int n, int k) {
+                                                                Out out, int n, int k) {
   using C = Nvfp4Rows<KC, R, W>;
   using S = typename C::S;  // assumes the longest rows (K = 2048 KC); shorter rows only end earlier
   const int kNibRow = k / 2, kScRow = k / 16;
@@ -205,66 +206,75 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
     }
     acc[r] = __builtin_fmaf(s1, a1, __builtin_fmaf(s0, a0, acc[r]));
   });
-  store_rows<R>(acc, y, row0, nrows, 1.f, lane);
+  store_rows<R>(acc, out, row0, nrows, 1.f, lane);
 }
 
-// One thread per 16 nibble bytes = 32 weights = two scale blocks.  The
-// flattened [M][K] index of a weight is twice its nibble-byte index (plus the
-// nibble), and its scale is byte (flattened index)/16 of the scale array,
-// because K is a multiple of 32.
-__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t* __restrict__ w,
-                                                            float* __restrict__ out,
-                                                            int64_t n_by_k) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t * 32 >= n_by_k) return;
-  const u32x4 v = *reinterpret_cast<const u32x4*>(w + 16 * t);
-  const unsigned sc = *reinterpret_cast<const uint16_t*>(w + n_by_k / 2 + 2 * t);
+// Row materialisation.  One thread per (output row, 16 nibble bytes) = 32
+// weights = two scale blocks; every weight e2m1 * |scale| is exact in fp32
+// (and in fp16 / bf16).
+template <typename T>
+__global__ __launch_bounds__(256) void nvfp4_rows_kernel(const uint8_t* __restrict__ w, int n, int k,
+                                                         const int32_t* __restrict__ rows, T* __restrict__ out,
+                                                         int bpr) {
+  const int j = blockIdx.x / bpr;
+  const int t = (blockIdx.x - j * bpr) * blockDim.x + threadIdx.x;
+  if (t >= k / 32) return;
+  T* const o = out + (int64_t)j * k + 32 * t;
+  const int r = source_row(rows, j, n);
+  if (r < 0) {
+    store16_nan(o);
+    store16_nan(o + 16);
+    return;
+  }
+  const u32x4 v = *reinterpret_cast<const u32x4*>(w + (int64_t)r * (k / 2) + 16 * t);
+  const unsigned sc =
+      *reinterpret_cast<const uint16_t*>(w + (int64_t)n * (k / 2) + (int64_t)r * (k / 16) + 2 * t);
   const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 0));
   const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 1));
   const unsigned q[4] = {v.x, v.y, v.z, v.w};
-  float o[32];
+  float a[16], b[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const f32x2 e = fp4x2_f32(q[j >> 2], j);
-    const float s = j < 8 ? s0 : s1;
-    o[2 * j] = e.x * s;
-    o[2 * j + 1] = e.y * s;
+  for (int i = 0; i < 8; ++i) {
+    const f32x2 e = fp4x2_f32(q[i >> 2], i);
+    a[2 * i] = e.x * s0;
+    a[2 * i + 1] = e.y * s0;
+    const f32x2 f = fp4x2_f32(q[(i + 8) >> 2], i + 8);
+    b[2 * i] = f.x * s1;
+    b[2 * i + 1] = f.y * s1;
   }
-  float* dst = out + 32 * t;
-#pragma unroll
-  for (int j = 0; j < 32; j += 4)
-    *reinterpret_cast<float4*>(dst + j) = make_float4(o[j], o[j + 1], o[j + 2], o[j + 3]);
+  store16(o, a);
+  store16(o + 16, b);
 }
 
-template <int R>
-static hipError_t launch_nvfp4_r(const void* w, const void* x, float* y, int64_t n, int64_t k,
+template <int R, typename Out>
+static hipError_t launch_nvfp4_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
                                  hipStream_t s) {
   const int kc = (int)((k + 2047) / 2048);
   const int kw = kc < QGEMV_WG_WAVES ? kc : QGEMV_WG_WAVES;
   const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
   const int rows_per_wg = rg * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(nvfp4_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
+  hipLaunchKernelGGL((nvfp4_gemv_kernel<R, Out>), dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
                      (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)k, kc, kw, rg);
   return hipGetLastError();
 }
 
-template <int KC, int R, int W>
-static hipError_t launch_nvfp4_rows_r(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+template <int KC, int R, int W, typename Out>
+static hipError_t launch_nvfp4_rows_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
   const int64_t rows_per_wg = (int64_t)W * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((nvfp4_gemv_rows_kernel<KC, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
+  hipLaunchKernelGGL((nvfp4_gemv_rows_kernel<KC, R, W, Out>), dim3((unsigned)grid), dim3(64 * W), 0, s,
                      (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)k);
   return hipGetLastError();
 }
 
-template <int KC>
-static hipError_t launch_nvfp4_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+template <int KC, typename Out>
+static hipError_t launch_nvfp4_rows(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
   constexpr int kRmax = largest_fitting_r([](int r) {
     return 8 * (((r * KC * 128 + 1023) / 1024) + r * KC) * 1024 + KC * 4096 <= 160 * 1024;
   });
   return dispatch_rows<kRmax>(n, [&](auto rc, auto wc) {
-    return launch_nvfp4_rows_r<KC, decltype(rc)::value, decltype(wc)::value>(w, x, y, n, k, s);
+    return launch_nvfp4_rows_r<KC, decltype(rc)::value, decltype(wc)::value, Out>(w, x, y, n, k, s);
   });
 }
 
@@ -272,30 +282,46 @@ static hipError_t launch_nvfp4_rows(const void* w, const void* x, float* y, int6
 #define QGEMV_NVFP4_IMPL 2  // 1: K-split kernel only, 2: row-streaming for K <= 16384
 #endif
 
-hipError_t launch_nvfp4_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
-                             hipStream_t s) {
+template <typename Out>
+static hipError_t launch_nvfp4_gemv_out(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
+                                      hipStream_t s) {
   if (QGEMV_NVFP4_IMPL == 2) {
     switch ((k + 2047) / 2048) {
-      case 1: return launch_nvfp4_rows<1>(w, x, y, n, k, s);
-      case 2: return launch_nvfp4_rows<2>(w, x, y, n, k, s);
-      case 3: return launch_nvfp4_rows<3>(w, x, y, n, k, s);
-      case 4: return launch_nvfp4_rows<4>(w, x, y, n, k, s);
-      case 5: return launch_nvfp4_rows<5>(w, x, y, n, k, s);
-      case 6: return launch_nvfp4_rows<6>(w, x, y, n, k, s);
-      case 7: return launch_nvfp4_rows<7>(w, x, y, n, k, s);
-      case 8: return launch_nvfp4_rows<8>(w, x, y, n, k, s);
+      case 1: return launch_nvfp4_rows<1, Out>(w, x, y, n, k, s);
+      case 2: return launch_nvfp4_rows<2, Out>(w, x, y, n, k, s);
+      case 3: return launch_nvfp4_rows<3, Out>(w, x, y, n, k, s);
+      case 4: return launch_nvfp4_rows<4, Out>(w, x, y, n, k, s);
+      case 5: return launch_nvfp4_rows<5, Out>(w, x, y, n, k, s);
+      case 6: return launch_nvfp4_rows<6, Out>(w, x, y, n, k, s);
+      case 7: return launch_nvfp4_rows<7, Out>(w, x, y, n, k, s);
+      case 8: return launch_nvfp4_rows<8, Out>(w, x, y, n, k, s);
       default: break;
     }
   }
-  return launch_nvfp4_r<QGEMV_NVFP4_R>(w, x, y, n, k, s);
+  return launch_nvfp4_r<QGEMV_NVFP4_R, Out>(w, x, y, n, k, s);
 }
 
-hipError_t launch_nvfp4_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
-  const int64_t threads = n * k / 32;
-  const int64_t grid = (threads + 255) / 256;
-  hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                     (const uint8_t*)w, out, n * k);
+hipError_t launch_nvfp4_gemv(const void* w, const void* x, const OutF32& y, int64_t n, int64_t k, hipStream_t s) {
+  return launch_nvfp4_gemv_out(w, x, y, n, k, s);
+}
+hipError_t launch_nvfp4_gemv(const void* w, const void* x, const OutEx& y, int64_t n, int64_t k, hipStream_t s) {
+  return launch_nvfp4_gemv_out(w, x, y, n, k, s);
+}
+
+template <typename T>
+static hipError_t launch_nvfp4_rows_t(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
+                                      void* out, hipStream_t s) {
+  const RowsGeom g = rows_geom(k / 32, nrows);
+  hipLaunchKernelGGL(nvfp4_rows_kernel<T>, dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w, (int)n,
+                     (int)k, rows, (T*)out, g.bpr);
   return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_get_rows(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
+                                 void* out, int dtype, hipStream_t s) {
+  if (dtype == kF16) return launch_nvfp4_rows_t<_Float16>(w, n, k, rows, nrows, out, s);
+  if (dtype == kBF16) return launch_nvfp4_rows_t<__bf16>(w, n, k, rows, nrows, out, s);
+  return launch_nvfp4_rows_t<float>(w, n, k, rows, nrows, out, s);
 }
 
 }  // namespace qgemv

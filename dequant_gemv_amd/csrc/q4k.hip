@@ -1,4 +1,4 @@
-// Q4_K fused dequantise + GEMV and fp32 dequantise for gfx950.
+// Q4_K fused dequantise + GEMV and row materialisation for gfx950.
 //
 // Block format ("Writing a high performant GEMV + dequant for Metal", sections
 // "What is a weight block?" and "Kernel code"): 144 bytes per 256 weights,
@@ -27,6 +27,7 @@
 // wave_reduce_rows) and across the K-chunk waves through LDS.
 #include "device.hpp"
 #include "launch.hpp"
+#include "rows.hpp"
 #include "stream.hpp"
 
 namespace qgemv {
@@ -75,9 +76,10 @@ struct Q4kScaleSel {
 constexpr int kQ4kBatchRows = 8;
 constexpr int kQ4kStage = kQ4kBatchRows * 8 * kQ4kBytes;  // 9216 bytes per wave
 
+template <typename Out>
 __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void q4k_gemv_lds_kernel(const uint8_t* __restrict__ w,
                                                                           const uint16_t* __restrict__ x,
-                                                                          float* __restrict__ y, int n, int nb,
+                                                                          Out out, int n, int nb,
                                                                           int kc, int kw, int rg) {
   __shared__ __attribute__((aligned(16))) unsigned char stage_all[QGEMV_WG_WAVES * kQ4kStage];
   __shared__ float red[QGEMV_WG_WAVES * kQ4kBatchRows];
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void q4k_gemv_lds_kernel(const
     float s = 0.f;
     for (int k = 0; k < kw; ++k) s += red[(g * kw + k) * R + r];
     const int row = blockIdx.x * rg * R + g * R + r;
-    if (row < n) y[row] = s * 0x1p24f;
+    if (row < n) out.put(row, s * 0x1p24f);
   }
 }
 
@@ -234,10 +236,10 @@ struct Q4kRows {
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
 
-template <int KC, int R, int W>
+template <int KC, int R, int W, typename Out>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __restrict__ w,
                                                                       const uint16_t* __restrict__ x,
-                                                                      float* __restrict__ y, int n, int nb) {
+                                                                      Out out, int n, int nb) {
   using C = Q4kRows<KC, R, W>;
   using S = typename C::S;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
@@ -336,21 +338,30 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
     else
       acc[r] += part;
   });
-  store_rows<R>(acc, y, row0, nrows, 0x1p24f, lane);
+  store_rows<R>(acc, out, row0, nrows, 0x1p24f, lane);
 }
 
-// One thread per (block, 16-byte nibble slice): 32 weights, written as the
-// correctly rounded fp32 of d*s*q - dmin*m (both products are exact in fp32,
-// so one fma rounds once).
-__global__ __launch_bounds__(256) void q4k_dequant_kernel(const uint8_t* __restrict__ w,
-                                                          float* __restrict__ out,
-                                                          int64_t nblocks) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= nblocks * 8) return;
-  const int64_t g = gid >> 3;
-  const int p = (int)(gid & 7), c = p >> 1, h = p & 1;
-  const u32x4 hdr = *reinterpret_cast<const u32x4*>(w + g * kQ4kBytes);
-  const u32x4 qv = *reinterpret_cast<const u32x4*>(w + g * kQ4kBytes + 16 + 16 * p);
+// Row materialisation.  One thread per (output row, block, 16-byte nibble
+// slice): 32 weights, each the correctly rounded fp32 of d*s*q - dmin*m (both
+// products are exact in fp32, so one fma rounds once), then converted to T.
+template <typename T>
+__global__ __launch_bounds__(256) void q4k_rows_kernel(const uint8_t* __restrict__ w, int n, int nb,
+                                                       const int32_t* __restrict__ rows, T* __restrict__ out,
+                                                       int bpr) {
+  const int j = blockIdx.x / bpr;
+  const int t = (blockIdx.x - j * bpr) * blockDim.x + threadIdx.x;
+  if (t >= nb * 8) return;
+  const int b = t >> 3, p = t & 7, c = p >> 1, h = p & 1;
+  T* const o = out + ((int64_t)j * nb + b) * 256 + 64 * c + 16 * h;
+  const int r = source_row(rows, j, n);
+  if (r < 0) {
+    store16_nan(o);
+    store16_nan(o + 32);
+    return;
+  }
+  const uint8_t* const blk = w + ((int64_t)r * nb + b) * kQ4kBytes;
+  const u32x4 hdr = *reinterpret_cast<const u32x4*>(blk);
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * p);
   const Q4kScaleSel sel(c);
   const unsigned sp = sel.scales(hdr.y, hdr.w), mp = sel.mins(hdr.z, hdr.w);
   const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
@@ -359,20 +370,17 @@ __global__ __launch_bounds__(256) void q4k_dequant_kernel(const uint8_t* __restr
   const unsigned q[4] = {qv.x, qv.y, qv.z, qv.w};
   float lo[16], hi[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const unsigned byte = (q[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-    lo[j] = __builtin_fmaf(dsa, (float)(byte & 15u), -dma);
-    hi[j] = __builtin_fmaf(dsb, (float)(byte >> 4), -dmb);
+  for (int i = 0; i < 16; ++i) {
+    const unsigned byte = (q[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    lo[i] = __builtin_fmaf(dsa, (float)(byte & 15u), -dma);
+    hi[i] = __builtin_fmaf(dsb, (float)(byte >> 4), -dmb);
   }
-  float* o = out + g * 256 + 64 * c + 16 * h;
-#pragma unroll
-  for (int j = 0; j < 16; j += 4) {
-    *reinterpret_cast<float4*>(o + j) = make_float4(lo[j], lo[j + 1], lo[j + 2], lo[j + 3]);
-    *reinterpret_cast<float4*>(o + 32 + j) = make_float4(hi[j], hi[j + 1], hi[j + 2], hi[j + 3]);
-  }
+  store16(o, lo);
+  store16(o + 32, hi);
 }
 
-static hipError_t launch_q4k_lds(const void* w, const void* x, float* y, int64_t n, int64_t k,
+template <typename Out>
+static hipError_t launch_q4k_lds(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
                                  hipStream_t s) {
   const int nb = (int)(k / 256);
   const int kc = (nb + 7) / 8;
@@ -380,7 +388,7 @@ static hipError_t launch_q4k_lds(const void* w, const void* x, float* y, int64_t
   const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
   const int rows_per_wg = rg * kQ4kBatchRows;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(q4k_gemv_lds_kernel, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
+  hipLaunchKernelGGL(q4k_gemv_lds_kernel<Out>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
                      (const uint8_t*)w, (const uint16_t*)x, y, (int)n, nb, kc, kw, rg);
   return hipGetLastError();
 }
@@ -389,39 +397,40 @@ static hipError_t launch_q4k_lds(const void* w, const void* x, float* y, int64_t
 // Row-streaming launch for the K-chunk counts it is instantiated for: R rows
 // per wave chosen so the grid is about one wave per SIMD (one-shot), capped by
 // the LDS stage; returns false when the shape has no instantiation.
-template <int KC, int R, int W>
-static hipError_t launch_q4k_rows_r(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+template <int KC, int R, int W, typename Out>
+static hipError_t launch_q4k_rows_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
   const int64_t rows_per_wg = (int64_t)W * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((q4k_gemv_rows_kernel<KC, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
+  hipLaunchKernelGGL((q4k_gemv_rows_kernel<KC, R, W, Out>), dim3((unsigned)grid), dim3(64 * W), 0, s,
                      (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)(k / 256));
   return hipGetLastError();
 }
 
-template <int KC>
-static hipError_t launch_q4k_rows_kc(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+template <int KC, typename Out>
+static hipError_t launch_q4k_rows_kc(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
   constexpr int kRmax = largest_fitting_r([](int r) {
     return 8 * ((r * KC * 8 * kQ4kBytes + 1023) / 1024) * 1024 + KC * 4096 <= 160 * 1024;
   });
   return dispatch_rows<kRmax>(n, [&](auto rc, auto wc) {
-    return launch_q4k_rows_r<KC, decltype(rc)::value, decltype(wc)::value>(w, x, y, n, k, s);
+    return launch_q4k_rows_r<KC, decltype(rc)::value, decltype(wc)::value, Out>(w, x, y, n, k, s);
   });
 }
 
 // Row streaming for K up to 16384 (at most 8 K-chunks of 2048); false when K
 // is larger (the K-split kernel takes it).
-static bool launch_q4k_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s,
+template <typename Out>
+static bool launch_q4k_rows(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s,
                             hipError_t* err) {
   const int kc = (int)((k / 256 + 7) / 8);
   switch (kc) {
-    case 1: *err = launch_q4k_rows_kc<1>(w, x, y, n, k, s); return true;
-    case 2: *err = launch_q4k_rows_kc<2>(w, x, y, n, k, s); return true;
-    case 3: *err = launch_q4k_rows_kc<3>(w, x, y, n, k, s); return true;
-    case 4: *err = launch_q4k_rows_kc<4>(w, x, y, n, k, s); return true;
-    case 5: *err = launch_q4k_rows_kc<5>(w, x, y, n, k, s); return true;
-    case 6: *err = launch_q4k_rows_kc<6>(w, x, y, n, k, s); return true;
-    case 7: *err = launch_q4k_rows_kc<7>(w, x, y, n, k, s); return true;
-    case 8: *err = launch_q4k_rows_kc<8>(w, x, y, n, k, s); return true;
+    case 1: *err = launch_q4k_rows_kc<1, Out>(w, x, y, n, k, s); return true;
+    case 2: *err = launch_q4k_rows_kc<2, Out>(w, x, y, n, k, s); return true;
+    case 3: *err = launch_q4k_rows_kc<3, Out>(w, x, y, n, k, s); return true;
+    case 4: *err = launch_q4k_rows_kc<4, Out>(w, x, y, n, k, s); return true;
+    case 5: *err = launch_q4k_rows_kc<5, Out>(w, x, y, n, k, s); return true;
+    case 6: *err = launch_q4k_rows_kc<6, Out>(w, x, y, n, k, s); return true;
+    case 7: *err = launch_q4k_rows_kc<7, Out>(w, x, y, n, k, s); return true;
+    case 8: *err = launch_q4k_rows_kc<8, Out>(w, x, y, n, k, s); return true;
     default: return false;
   }
 }
@@ -431,8 +440,9 @@ static bool launch_q4k_rows(const void* w, const void* x, float* y, int64_t n, i
 #define QGEMV_Q4K_IMPL 2
 #endif
 
-hipError_t launch_q4k_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
-                           hipStream_t s) {
+template <typename Out>
+static hipError_t launch_q4k_gemv_out(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
+                                      hipStream_t s) {
   if (QGEMV_Q4K_IMPL == 2) {
     hipError_t e = hipSuccess;
     if (launch_q4k_rows(w, x, y, n, k, s, &e)) return e;
@@ -440,13 +450,27 @@ hipError_t launch_q4k_gemv(const void* w, const void* x, float* y, int64_t n, in
   return launch_q4k_lds(w, x, y, n, k, s);
 }
 
-hipError_t launch_q4k_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
-  const int64_t nblocks = n * (k / 256);
-  const int64_t threads = nblocks * 8;
-  const int64_t grid = (threads + 255) / 256;
-  hipLaunchKernelGGL(q4k_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                     (const uint8_t*)w, out, nblocks);
+hipError_t launch_q4k_gemv(const void* w, const void* x, const OutF32& y, int64_t n, int64_t k, hipStream_t s) {
+  return launch_q4k_gemv_out(w, x, y, n, k, s);
+}
+hipError_t launch_q4k_gemv(const void* w, const void* x, const OutEx& y, int64_t n, int64_t k, hipStream_t s) {
+  return launch_q4k_gemv_out(w, x, y, n, k, s);
+}
+
+template <typename T>
+static hipError_t launch_q4k_rows_t(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
+                                    void* out, hipStream_t s) {
+  const RowsGeom g = rows_geom(k / 256 * 8, nrows);
+  hipLaunchKernelGGL(q4k_rows_kernel<T>, dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w, (int)n,
+                     (int)(k / 256), rows, (T*)out, g.bpr);
   return hipGetLastError();
+}
+
+hipError_t launch_q4k_get_rows(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows, void* out,
+                               int dtype, hipStream_t s) {
+  if (dtype == kF16) return launch_q4k_rows_t<_Float16>(w, n, k, rows, nrows, out, s);
+  if (dtype == kBF16) return launch_q4k_rows_t<__bf16>(w, n, k, rows, nrows, out, s);
+  return launch_q4k_rows_t<float>(w, n, k, rows, nrows, out, s);
 }
 
 }  // namespace qgemv

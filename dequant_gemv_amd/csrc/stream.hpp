@@ -6,6 +6,7 @@
 // are summed across the wave with DPP and stored by lanes 48.. .
 #pragma once
 #include "device.hpp"
+#include "epilogue.hpp"
 
 namespace qgemv {
 
@@ -61,10 +62,10 @@ __device__ __forceinline__ void load_shared_pieces(__amdgpu_buffer_rsrc_t r, uns
   }
 }
 
-// Sum R per-lane row partials across the wave and store row j (< nrows) of
-// y[row0 ..] from lane 48 + j, times `scale`.
-template <int R>
-__device__ __forceinline__ void store_rows(float (&acc)[R], float* __restrict__ y, int row0, int nrows, float scale,
+// Sum R per-lane row partials across the wave and hand row j (< nrows),
+// times `scale`, to the output stage as row row0 + j from lane 48 + j.
+template <int R, typename Out>
+__device__ __forceinline__ void store_rows(float (&acc)[R], const Out& out, int row0, int nrows, float scale,
                                            int lane) {
   static_assert(R >= 1 && R <= 16, "one row per lane of the last 16-lane row");
   wave_reduce_dpp<R>(acc);
@@ -72,7 +73,7 @@ __device__ __forceinline__ void store_rows(float (&acc)[R], float* __restrict__ 
   float t = acc[0];
 #pragma unroll
   for (int s = 1; s < R; ++s) t = j == s ? acc[s] : t;
-  if (lane >= 48 && j < nrows) y[row0 + j] = t * scale;
+  if (lane >= 48 && j < nrows) out.put(row0 + j, t * scale);
 }
 
 // Shape -> (R rows per wave, W waves per workgroup) of a row-streaming

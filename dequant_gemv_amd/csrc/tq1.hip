@@ -1,4 +1,4 @@
-// TQ1_0 fused dequantise + GEMV and fp32 dequantise for gfx950.
+// TQ1_0 fused dequantise + GEMV and row materialisation for gfx950.
 //
 // Format ("metal: TQ1_0 kernel performance", sections 1 and 2): 54 bytes per
 // 256 weights, qs[48] (five base-3 digits per byte) | qh[4] (four digits per
@@ -31,6 +31,7 @@
 // ds_bpermute.  sum x*(t-1) = sum x*t - sum x, the second term precomputed.
 #include "device.hpp"
 #include "launch.hpp"
+#include "rows.hpp"
 #include "stream.hpp"
 
 namespace qgemv {
@@ -75,10 +76,10 @@ __device__ __forceinline__ void tq1_digits(unsigned B, unsigned (&D)[5]) {
   for (int k = 1; k <= 4; ++k) D[k] = as_u32(F[k + 1] + F[k] * (u16v2){0xFFFD, 0xFFFD});
 }
 
-template <int R>
+template <int R, typename Out>
 __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void tq1_gemv_kernel(const uint8_t* __restrict__ w,
                                                        const uint16_t* __restrict__ x,
-                                                       float* __restrict__ y, int n, int nb,
+                                                       Out out, int n, int nb,
                                                        int kc, int kw, int rg) {
   __shared__ float red[16 * 16];
   const int lane = __lane_id();
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void tq1_gemv_kernel(const uin
     float s = 0.f;
     for (int kk = 0; kk < kw; ++kk) s += red[(g * kw + kk) * R + r];
     const int row = blockIdx.x * rg * R + g * R + r;
-    if (row < n) y[row] = s;
+    if (row < n) out.put(row, s);
   }
 }
 
@@ -219,10 +220,10 @@ struct Tq1Rows {
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
 
-template <int KS, int R, int W>
+template <int KS, int R, int W, typename Out>
 __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __restrict__ w,
                                                               const uint16_t* __restrict__ x,
-                                                              float* __restrict__ y, int n, int nb) {
+                                                              Out out, int n, int nb) {
   using C = Tq1Rows<KS, R, W>;
   using S = typename C::S;  // assumes full segments; a short last segment only ends earlier
   const int kRowBytes = nb * kTq1Bytes;
@@ -328,23 +329,31 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
     const float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0[sg]), acc[r]);
     acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1[sg]), t);
   });
-  store_rows<R>(acc, y, row0, nrows, 1.f, lane);
+  store_rows<R>(acc, out, row0, nrows, 1.f, lane);
 }
 
-// One thread per (block, run of 16 elements il): elements 16 il .. 16 il + 15.
-// For il < 10 they are digit il/2 of qs[16 (il%2) + e]; for il < 15 digit
-// il-10 of qs[32 + e]; il = 15 is digit e/4 of qh[e%4] (the section-2 element
-// order of the TQ1_0 page).  Weight = d * (digit - 1), exact in fp32.
-__global__ __launch_bounds__(256) void tq1_dequant_kernel(const uint8_t* __restrict__ w,
-                                                          float* __restrict__ out,
-                                                          int64_t nblocks) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nblocks * 16) return;
-  const int64_t g = t >> 4;
-  const int il = (int)(t & 15);
-  const uint8_t* b = w + g * kTq1Bytes;
+// Row materialisation.  One thread per (output row, block, run of 16
+// elements il): elements 16 il .. 16 il + 15.  For il < 10 they are digit il/2
+// of qs[16 (il%2) + e]; for il < 15 digit il-10 of qs[32 + e]; il = 15 is
+// digit e/4 of qh[e%4] (the section-2 element order of the TQ1_0 page).
+// Weight = d * (digit - 1), exact in fp32 (and in fp16).
+template <typename T>
+__global__ __launch_bounds__(256) void tq1_rows_kernel(const uint8_t* __restrict__ w, int n, int nb,
+                                                       const int32_t* __restrict__ rows, T* __restrict__ out,
+                                                       int bpr) {
+  const int j = blockIdx.x / bpr;
+  const int t = (blockIdx.x - j * bpr) * blockDim.x + threadIdx.x;
+  if (t >= nb * 16) return;
+  const int blk_i = t >> 4, il = t & 15;
+  T* const o = out + ((int64_t)j * nb + blk_i) * 256 + 16 * il;
+  const int r = source_row(rows, j, n);
+  if (r < 0) {
+    store16_nan(o);
+    return;
+  }
+  const uint8_t* const b = w + ((int64_t)r * nb + blk_i) * kTq1Bytes;
   const float d = (float)__builtin_bit_cast(_Float16, (unsigned short)(b[52] | (b[53] << 8)));
-  float o[16];
+  float v[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     int byte, k;
@@ -352,19 +361,16 @@ __global__ __launch_bounds__(256) void tq1_dequant_kernel(const uint8_t* __restr
     else if (il < 15) { byte = 32 + e; k = il - 10; }
     else { byte = 48 + (e & 3); k = e >> 2; }
     int p = 1;
-    for (int j = 0; j < k; ++j) p *= 3;
-    const int v = b[byte];
-    const int digit = (p * 3 * v) / 256 - 3 * ((p * v) / 256);
-    o[e] = d * (float)(digit - 1);
+    for (int i = 0; i < k; ++i) p *= 3;
+    const int q = b[byte];
+    const int digit = (p * 3 * q) / 256 - 3 * ((p * q) / 256);
+    v[e] = d * (float)(digit - 1);
   }
-  float* dst = out + g * 256 + 16 * il;
-#pragma unroll
-  for (int e = 0; e < 16; e += 4)
-    *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+  store16(o, v);
 }
 
-template <int R>
-static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n, int64_t k,
+template <int R, typename Out>
+static hipError_t launch_tq1_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
                                hipStream_t s) {
   const int nb = (int)(k / 256);
   const int kc = (nb + kTq1SegBlocks - 1) / kTq1SegBlocks;
@@ -372,27 +378,27 @@ static hipError_t launch_tq1_r(const void* w, const void* x, float* y, int64_t n
   const int rg = kw >= QGEMV_WG_WAVES ? 1 : QGEMV_WG_WAVES / kw;
   const int rows_per_wg = rg * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(tq1_gemv_kernel<R>, dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
+  hipLaunchKernelGGL((tq1_gemv_kernel<R, Out>), dim3((unsigned)grid), dim3(64 * kw * rg), 0, s,
                      (const uint8_t*)w, (const uint16_t*)x, y, (int)n, nb, kc, kw, rg);
   return hipGetLastError();
 }
 
-template <int KS, int R, int W>
-static hipError_t launch_tq1_rows_r(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+template <int KS, int R, int W, typename Out>
+static hipError_t launch_tq1_rows_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
   const int64_t rows_per_wg = (int64_t)W * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((tq1_gemv_rows_kernel<KS, R, W>), dim3((unsigned)grid), dim3(64 * W), 0, s,
+  hipLaunchKernelGGL((tq1_gemv_rows_kernel<KS, R, W, Out>), dim3((unsigned)grid), dim3(64 * W), 0, s,
                      (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)(k / 256));
   return hipGetLastError();
 }
 
-template <int KS>
-static hipError_t launch_tq1_rows(const void* w, const void* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+template <int KS, typename Out>
+static hipError_t launch_tq1_rows(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
   constexpr int kRmax = largest_fitting_r([](int r) {
     return 8 * ((r * KS * kTq1SegBytes + 1023) / 1024) * 1024 + KS * 8192 + 16 <= 160 * 1024;
   });
   return dispatch_rows<kRmax>(n, [&](auto rc, auto wc) {
-    return launch_tq1_rows_r<KS, decltype(rc)::value, decltype(wc)::value>(w, x, y, n, k, s);
+    return launch_tq1_rows_r<KS, decltype(rc)::value, decltype(wc)::value, Out>(w, x, y, n, k, s);
   });
 }
 
@@ -400,22 +406,37 @@ static hipError_t launch_tq1_rows(const void* w, const void* x, float* y, int64_
 #define QGEMV_TQ1_IMPL 2  // 1: K-split kernel only, 2: row-streaming for K % 2048 == 0, K <= 8192
 #endif
 
-hipError_t launch_tq1_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k,
-                           hipStream_t s) {
+template <typename Out>
+static hipError_t launch_tq1_gemv_out(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
+                                      hipStream_t s) {
   if (QGEMV_TQ1_IMPL == 2 && k % 2048 == 0) {
-    if (k <= 4096) return launch_tq1_rows<1>(w, x, y, n, k, s);
-    if (k <= 8192) return launch_tq1_rows<2>(w, x, y, n, k, s);
+    if (k <= 4096) return launch_tq1_rows<1, Out>(w, x, y, n, k, s);
+    if (k <= 8192) return launch_tq1_rows<2, Out>(w, x, y, n, k, s);
   }
-  return launch_tq1_r<QGEMV_TQ1_R>(w, x, y, n, k, s);
+  return launch_tq1_r<QGEMV_TQ1_R, Out>(w, x, y, n, k, s);
 }
 
-hipError_t launch_tq1_dequant(const void* w, float* out, int64_t n, int64_t k, hipStream_t s) {
-  const int64_t nblocks = n * (k / 256);
-  const int64_t threads = nblocks * 16;
-  const int64_t grid = (threads + 255) / 256;
-  hipLaunchKernelGGL(tq1_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                     (const uint8_t*)w, out, nblocks);
+hipError_t launch_tq1_gemv(const void* w, const void* x, const OutF32& y, int64_t n, int64_t k, hipStream_t s) {
+  return launch_tq1_gemv_out(w, x, y, n, k, s);
+}
+hipError_t launch_tq1_gemv(const void* w, const void* x, const OutEx& y, int64_t n, int64_t k, hipStream_t s) {
+  return launch_tq1_gemv_out(w, x, y, n, k, s);
+}
+
+template <typename T>
+static hipError_t launch_tq1_rows_t(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
+                                    void* out, hipStream_t s) {
+  const RowsGeom g = rows_geom(k / 256 * 16, nrows);
+  hipLaunchKernelGGL(tq1_rows_kernel<T>, dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w, (int)n,
+                     (int)(k / 256), rows, (T*)out, g.bpr);
   return hipGetLastError();
+}
+
+hipError_t launch_tq1_get_rows(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows, void* out,
+                               int dtype, hipStream_t s) {
+  if (dtype == kF16) return launch_tq1_rows_t<_Float16>(w, n, k, rows, nrows, out, s);
+  if (dtype == kBF16) return launch_tq1_rows_t<__bf16>(w, n, k, rows, nrows, out, s);
+  return launch_tq1_rows_t<float>(w, n, k, rows, nrows, out, s);
 }
 
 }  // namespace qgemv

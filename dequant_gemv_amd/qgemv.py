@@ -20,13 +20,28 @@ QGEMV_E_SHAPE = -2
 QGEMV_E_ALIGN = -3
 QGEMV_E_HIP = -4
 QGEMV_E_ALIAS = -5
+QGEMV_E_DTYPE = -6
+
+# element type codes
+QGEMV_F32 = 0
+QGEMV_F16 = 1
+QGEMV_BF16 = 2
+DTYPE_CODE = {"f32": QGEMV_F32, "f16": QGEMV_F16, "bf16": QGEMV_BF16}
 
 # Entry points declared in include/qgemv.h.
-GEMV_SYMBOLS = ("qgemv_q4k", "qgemv_nvfp4", "qgemv_tq1")
+GEMV_SYMBOLS = ("qgemv_q4k", "qgemv_nvfp4", "qgemv_tq1", "qgemv_f16", "qgemv_bf16")
+GEMV_EX_SYMBOLS = ("qgemv_q4k_ex", "qgemv_nvfp4_ex", "qgemv_tq1_ex", "qgemv_f16_ex", "qgemv_bf16_ex")
 DEQUANT_SYMBOLS = ("qdequant_q4k", "qdequant_nvfp4", "qdequant_tq1")
-ALL_SYMBOLS = GEMV_SYMBOLS + DEQUANT_SYMBOLS + (
+ROWS_SYMBOLS = ("qget_rows_q4k", "qget_rows_nvfp4", "qget_rows_tq1")
+ALL_SYMBOLS = GEMV_SYMBOLS + GEMV_EX_SYMBOLS + DEQUANT_SYMBOLS + ROWS_SYMBOLS + (
     "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror", "qgemv_last_hip_error",
     "qgemv_build_id")
+
+
+class Epilogue(ctypes.Structure):
+    """struct qgemv_epilogue: y = alpha * v + beta * c, stored as y_dtype."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("c", ctypes.c_void_p),
+                ("c_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32)]
 
 
 class QgemvError(RuntimeError):
@@ -47,10 +62,18 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [P, P, P, I64, I64, P]
+    for name in GEMV_EX_SYMBOLS:
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, P, I64, I64, ctypes.POINTER(Epilogue), P]
     for name in DEQUANT_SYMBOLS:
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [P, P, I64, I64, P]
+    for name in ROWS_SYMBOLS:
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [P, I64, I64, P, I64, P, ctypes.c_int32, P]
     lib.qgemv_read_ceiling.restype = ctypes.c_int
     lib.qgemv_read_ceiling.argtypes = [P, I64, P, P]
     lib.qgemv_read_sink_len.restype = ctypes.c_int64
@@ -117,6 +140,80 @@ def qgemv_tq1(w, x, y, M, K, stream=None):
     return _gemv("qgemv_tq1", w, x, y, M, K, stream)
 
 
+def qgemv_f16(w, x, y, M, K, stream=None):
+    """y[M] (fp32) = x[K] (fp16) . W^T with W [M][K] fp16, enqueued on `stream`."""
+    return _gemv("qgemv_f16", w, x, y, M, K, stream)
+
+
+def qgemv_bf16(w, x, y, M, K, stream=None):
+    """y[M] (fp32) = x[K] (bf16) . W^T with W [M][K] bf16, enqueued on `stream`."""
+    return _gemv("qgemv_bf16", w, x, y, M, K, stream)
+
+
+def dtype_code(t) -> int:
+    """Element-type code of a torch tensor (fp32 / fp16 / bf16)."""
+    import torch
+
+    codes = {torch.float32: QGEMV_F32, torch.float16: QGEMV_F16, torch.bfloat16: QGEMV_BF16}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported element type {t.dtype}")
+    return codes[t.dtype]
+
+
+def _gemv_ex(name, w, x, y, M, K, alpha, beta, c, stream):
+    ep = Epilogue(float(alpha), float(beta), _addr(c) if c is not None else None,
+                  dtype_code(c) if c is not None else QGEMV_F32, dtype_code(y))
+    _check(getattr(_lib, name)(_addr(w), _addr(x), _addr(y), int(M), int(K), ctypes.byref(ep),
+                               _stream(stream)), name)
+    return y
+
+
+def qgemv_q4k_ex(w, x, y, M, K, alpha=1.0, beta=0.0, c=None, stream=None):
+    """y = alpha * (x . dequant_Q4_K(w)^T) + beta * c in y's element type."""
+    return _gemv_ex("qgemv_q4k_ex", w, x, y, M, K, alpha, beta, c, stream)
+
+
+def qgemv_nvfp4_ex(w, x, y, M, K, alpha=1.0, beta=0.0, c=None, stream=None):
+    return _gemv_ex("qgemv_nvfp4_ex", w, x, y, M, K, alpha, beta, c, stream)
+
+
+def qgemv_tq1_ex(w, x, y, M, K, alpha=1.0, beta=0.0, c=None, stream=None):
+    return _gemv_ex("qgemv_tq1_ex", w, x, y, M, K, alpha, beta, c, stream)
+
+
+def qgemv_f16_ex(w, x, y, M, K, alpha=1.0, beta=0.0, c=None, stream=None):
+    return _gemv_ex("qgemv_f16_ex", w, x, y, M, K, alpha, beta, c, stream)
+
+
+def qgemv_bf16_ex(w, x, y, M, K, alpha=1.0, beta=0.0, c=None, stream=None):
+    return _gemv_ex("qgemv_bf16_ex", w, x, y, M, K, alpha, beta, c, stream)
+
+
+def _get_rows(name, w, M, K, rows, nrows, out, stream):
+    if rows is not None and not isinstance(rows, int):
+        import torch
+
+        if rows.dtype != torch.int32:
+            raise ValueError("row indices must be an int32 tensor")
+    _check(getattr(_lib, name)(_addr(w), int(M), int(K), _addr(rows), int(nrows), _addr(out),
+                               dtype_code(out), _stream(stream)), name)
+    return out
+
+
+def qget_rows_q4k(w, M, K, rows, nrows, out, stream=None):
+    """out[nrows][K] = rows `rows` (int32 device tensor, or None for 0..nrows-1)
+    of dequant_Q4_K(w), in out's element type."""
+    return _get_rows("qget_rows_q4k", w, M, K, rows, nrows, out, stream)
+
+
+def qget_rows_nvfp4(w, M, K, rows, nrows, out, stream=None):
+    return _get_rows("qget_rows_nvfp4", w, M, K, rows, nrows, out, stream)
+
+
+def qget_rows_tq1(w, M, K, rows, nrows, out, stream=None):
+    return _get_rows("qget_rows_tq1", w, M, K, rows, nrows, out, stream)
+
+
 def _dequant(name, w, out, M, K, stream):
     _check(getattr(_lib, name)(_addr(w), _addr(out), int(M), int(K), _stream(stream)), name)
     return out
@@ -153,8 +250,11 @@ def qgemv_strerror(code: int) -> str:
 
 
 # Convenience: allocate y / out with torch and dispatch by format name.
-GEMV = {"q4k": qgemv_q4k, "nvfp4": qgemv_nvfp4, "tq1": qgemv_tq1}
+GEMV = {"q4k": qgemv_q4k, "nvfp4": qgemv_nvfp4, "tq1": qgemv_tq1, "f16": qgemv_f16, "bf16": qgemv_bf16}
+GEMV_EX = {"q4k": qgemv_q4k_ex, "nvfp4": qgemv_nvfp4_ex, "tq1": qgemv_tq1_ex, "f16": qgemv_f16_ex,
+           "bf16": qgemv_bf16_ex}
 DEQUANT = {"q4k": qdequant_q4k, "nvfp4": qdequant_nvfp4, "tq1": qdequant_tq1}
+GET_ROWS = {"q4k": qget_rows_q4k, "nvfp4": qget_rows_nvfp4, "tq1": qget_rows_tq1}
 
 
 def gemv(fmt: str, w, x, M: int, K: int, y=None, stream=None):
@@ -171,3 +271,28 @@ def dequant(fmt: str, w, M: int, K: int, out=None, stream=None):
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=w.device)
     return DEQUANT[fmt](w, out, M, K, stream)
+
+
+def _torch_dtype(name: str):
+    import torch
+
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+def gemv_ex(fmt: str, w, x, M: int, K: int, alpha=1.0, beta=0.0, c=None, y_dtype="f32", y=None,
+            stream=None):
+    import torch
+
+    if y is None:
+        y = torch.empty(M, dtype=_torch_dtype(y_dtype), device=w.device)
+    return GEMV_EX[fmt](w, x, y, M, K, alpha, beta, c, stream)
+
+
+def get_rows(fmt: str, w, M: int, K: int, rows=None, nrows=None, dtype="f16", out=None, stream=None):
+    import torch
+
+    if nrows is None:
+        nrows = M if rows is None else rows.numel()
+    if out is None:
+        out = torch.empty((nrows, K), dtype=_torch_dtype(dtype), device=w.device)
+    return GET_ROWS[fmt](w, M, K, rows, nrows, out, stream)

@@ -1,18 +1,20 @@
 /*
  * qgemv.h — C ABI of the MI355X (gfx950) fused dequantise + GEMV library.
  *
- * Every call computes, for ONE activation row,
- *     y[r] = sum_{i<K} x[i] * dequant(W)[r][i]        r = 0 .. M-1
- * i.e. y = x . dequant(W)^T with alpha = 1 and beta = 0 ("Writing a high
- * performant GEMV + dequant for Metal", section "What is a GEMV"), or
- * materialises dequant(W) as fp32.
+ * Every GEMV call computes, for ONE activation row,
+ *     v[r] = sum_{i<K} x[i] * dequant(W)[r][i]        r = 0 .. M-1
+ * i.e. v = x . dequant(W)^T ("Writing a high performant GEMV + dequant for
+ * Metal", section "What is a GEMV").  The plain calls store y = v in fp32
+ * (alpha = 1, beta = 0); the _ex calls apply the general output stage
+ * y = alpha v + beta c in fp32, fp16 or bf16.  The row calls materialise rows
+ * of dequant(W) as fp32, fp16 or bf16.
  *
  * Conventions shared by every entry point
  *   M       number of rows of W = number of outputs (the batch is always 1).
  *   K       reduction length (elements per row of W and of x).
  *   Layout  W is row-major with K contiguous, in the format's packed blocks;
- *           x is K contiguous 16-bit values; y is M contiguous fp32 values;
- *           dequant outputs are M*K contiguous fp32 values, row-major.
+ *           x is K contiguous 16-bit values; y is M contiguous values;
+ *           materialised rows are contiguous and row-major.
  *   Memory  every pointer is DEVICE memory owned by the caller (e.g. torch
  *           tensors).  The library allocates nothing, keeps no per-call state
  *           and never synchronises.  y must not overlap x or W.
@@ -22,7 +24,8 @@
  *           argument returns a negative QGEMV_E_* code and enqueues nothing.
  *           A failed launch returns QGEMV_E_HIP.  The library never prints or
  *           aborts.  M == 0 is a successful no-op.
- *   Alignment  W, x and dequant outputs must be 16-byte aligned; y 4-byte.
+ *   Alignment  W, x and materialised rows must be 16-byte aligned; y and c
+ *              to their element size.
  *   Threads    calls are thread-safe (no global mutable state).
  */
 #ifndef QGEMV_H
@@ -42,8 +45,13 @@ enum {
   QGEMV_E_SHAPE = -2, /* M < 0, K <= 0, K not a multiple of the block, or sizes overflow */
   QGEMV_E_ALIGN = -3, /* a pointer is not aligned as required */
   QGEMV_E_HIP = -4,   /* the HIP runtime rejected the launch */
-  QGEMV_E_ALIAS = -5  /* the output overlaps an input */
+  QGEMV_E_ALIAS = -5, /* the output overlaps an input */
+  QGEMV_E_DTYPE = -6  /* an element-type code is not one of QGEMV_F32 / QGEMV_F16 / QGEMV_BF16 */
 };
+
+/* Element types of epilogue vectors and materialised rows: fp32, IEEE binary16
+ * and bfloat16.  Conversions to the 16-bit types round to nearest even. */
+enum { QGEMV_F32 = 0, QGEMV_F16 = 1, QGEMV_BF16 = 2 };
 
 /* Q4_K ("Writing a high performant GEMV + dequant for Metal", sections "What is
  * a weight block?", "Compute", "Kernel code"): K % 256 == 0; each row holds K/256
@@ -72,8 +80,69 @@ int qgemv_nvfp4(const void* w, const void* x_bf16, float* y, int64_t M, int64_t 
 int qgemv_tq1(const void* w, const void* x_f16, float* y, int64_t M, int64_t K,
               struct ihipStream_t* stream);
 
+/* General output stage ("Writing a high performant GEMV + dequant for Metal",
+ * section "What is a GEMV": y = alpha * x . W^T + beta * c; that page's kernel
+ * writes fp16 y, the Mojo fp4_gemv page ends in a final cast):
+ *     y[r] = alpha * v_r + beta * c[r]      v_r = x . dequant(W)[r] in fp32
+ * evaluated in fp32 (one fma for the beta term) and stored as y_dtype.
+ *   alpha, beta  scalars (host values copied at the call).
+ *   c            M elements of c_dtype in device memory, read only when
+ *                beta != 0 (it may then be NULL).  c may be y itself when
+ *                c_dtype == y_dtype (in place: y = alpha v + beta y); any other
+ *                overlap of c with y returns QGEMV_E_ALIAS.
+ *   y            M elements of y_dtype (aligned to its size).
+ * A NULL epilogue pointer means alpha = 1, beta = 0, fp32 y. */
+typedef struct qgemv_epilogue {
+  float alpha;
+  float beta;
+  const void* c;
+  int32_t c_dtype;
+  int32_t y_dtype;
+} qgemv_epilogue;
+
+/* The three GEMVs above with the general output stage; W, x, M, K, stream and
+ * the errors as for the plain calls, plus QGEMV_E_DTYPE for a bad type code. */
+int qgemv_q4k_ex(const void* w, const void* x_f16, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                 struct ihipStream_t* stream);
+int qgemv_nvfp4_ex(const void* w, const void* x_bf16, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                   struct ihipStream_t* stream);
+int qgemv_tq1_ex(const void* w, const void* x_f16, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                 struct ihipStream_t* stream);
+
+/* Dense GEMV, the uncompressed comparison point of the Mojo fp4_gemv page (its
+ * NVFP4 GEMV against a bf16 GEMV of the same shape): W is [M][K] row-major in
+ * the activations' type, fp16 for qgemv_f16 and bf16 for qgemv_bf16.
+ * 0 < K <= 65536 and K % 8 == 0 (rows start 16-byte aligned); W occupies
+ * 2*M*K bytes.  Other conventions as above; the _ex forms take the general
+ * output stage. */
+int qgemv_f16(const void* w, const void* x_f16, float* y, int64_t M, int64_t K, struct ihipStream_t* stream);
+int qgemv_bf16(const void* w, const void* x_bf16, float* y, int64_t M, int64_t K, struct ihipStream_t* stream);
+int qgemv_f16_ex(const void* w, const void* x_f16, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                 struct ihipStream_t* stream);
+int qgemv_bf16_ex(const void* w, const void* x_bf16, void* y, int64_t M, int64_t K, const qgemv_epilogue* ep,
+                  struct ihipStream_t* stream);
+
+/* Row materialisation (GET_ROWS; the dequantize template of "metal: TQ1_0
+ * kernel performance", section "Prefill", and the Mojo fp4_gemv page's
+ * dequant): out[j][0..K) = row rows[j] of dequant(W) for j < nrows, each
+ * weight rounded to fp32 and then to out_dtype.
+ *   w, M, K   the packed matrix, as for the GEMVs of the same format.
+ *   rows      nrows int32 row indices in device memory, or NULL for rows
+ *             0..nrows-1 (then nrows <= M).  An index outside [0, M) gives a
+ *             row of quiet NaNs (sign bit clear): indices are device data and
+ *             are not checked on the host.
+ *   out       nrows*K elements of out_dtype, 16-byte aligned, not overlapping
+ *             W or rows.
+ * nrows == 0 is a successful no-op. */
+int qget_rows_q4k(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
+                  int32_t out_dtype, struct ihipStream_t* stream);
+int qget_rows_nvfp4(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
+                    int32_t out_dtype, struct ihipStream_t* stream);
+int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
+                  int32_t out_dtype, struct ihipStream_t* stream);
+
 /* fp32 materialisation out[M][K] of the same formats (same W conventions as
- * above).  Each value is the correctly rounded fp32 of the exact weight, which
+ * above; the same as qget_rows_* with rows = NULL, nrows = M, QGEMV_F32).  Each value is the correctly rounded fp32 of the exact weight, which
  * for these formats is the exact weight itself whenever it is representable
  * (the bit-exact reference for the GEMVs; Mojo module "fp4_gemv", TQ1_0 PR
  * section "Correctness"). */

@@ -25,7 +25,7 @@ def q():
 
 def test_header_symbols_exported(q):
     names = _header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 21, names
     lib = q.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -39,7 +39,7 @@ def test_build_id_matches_sources(q):
 
 
 def test_strerror(q):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert q.qgemv_strerror(code)
     assert "unknown" in q.qgemv_strerror(42)
 
@@ -47,15 +47,19 @@ def test_strerror(q):
 A = 0x7F0000000000  # a 16-byte aligned fake device address, never dereferenced
 
 
-@pytest.mark.parametrize("name,kmul", [("qgemv_q4k", 256), ("qgemv_nvfp4", 32), ("qgemv_tq1", 256)])
-def test_gemv_validation(q, name, kmul):
+GEMVS = [("qgemv_q4k", 256, 1 << 24), ("qgemv_nvfp4", 32, 1 << 24), ("qgemv_tq1", 256, 1 << 24),
+         ("qgemv_f16", 8, 65536), ("qgemv_bf16", 8, 65536)]
+
+
+@pytest.mark.parametrize("name,kmul,kmax", GEMVS)
+def test_gemv_validation(q, name, kmul, kmax):
     f = getattr(q.lib(), name)
     W, X, Y = A, A + (1 << 32), A + (2 << 32)
     assert f(W, X, Y, -1, kmul, None) == q.QGEMV_E_SHAPE
     assert f(W, X, Y, 4, 0, None) == q.QGEMV_E_SHAPE
-    assert f(W, X, Y, 4, kmul + 16, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 4, kmul + kmul // 2, None) == q.QGEMV_E_SHAPE
     assert f(W, X, Y, 4, -kmul, None) == q.QGEMV_E_SHAPE
-    assert f(W, X, Y, 4, (1 << 24) + kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 4, kmax + kmul, None) == q.QGEMV_E_SHAPE
     assert f(W, X, Y, 1 << 31, kmul, None) == q.QGEMV_E_SHAPE
     assert f(W, X, Y, 0, kmul, None) == q.QGEMV_OK  # empty: no-op, no launch
     assert f(None, X, Y, 4, kmul, None) == q.QGEMV_E_NULL
@@ -66,6 +70,45 @@ def test_gemv_validation(q, name, kmul):
     assert f(W, X, Y + 2, 4, kmul, None) == q.QGEMV_E_ALIGN
     assert f(W, X, W + 16, 4, kmul, None) == q.QGEMV_E_ALIAS
     assert f(W, X, X, 4, kmul, None) == q.QGEMV_E_ALIAS
+
+
+@pytest.mark.parametrize("name,kmul,kmax", GEMVS)
+def test_gemv_ex_validation(q, name, kmul, kmax):
+    f = getattr(q.lib(), name + "_ex")
+    E = q.Epilogue
+    W, X, Y, C = A, A + (1 << 32), A + (2 << 32), A + (3 << 32)
+    ok = E(1.0, 0.0, None, q.QGEMV_F32, q.QGEMV_F32)
+    assert f(W, X, Y, 4, kmax + kmul, ctypes.byref(ok), None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 4, kmul, ctypes.byref(E(1.0, 0.0, None, 0, 3)), None) == q.QGEMV_E_DTYPE
+    assert f(W, X, Y, 4, kmul, ctypes.byref(E(1.0, 1.0, C, -1, 0)), None) == q.QGEMV_E_DTYPE
+    # c's type is irrelevant (and c not read) when beta == 0
+    assert f(W, X, Y, 0, kmul, ctypes.byref(E(1.0, 0.0, None, 7, 0)), None) == q.QGEMV_OK
+    assert f(W, X, Y, 0, kmul, None, None) == q.QGEMV_OK  # NULL epilogue = plain
+    assert f(W, X, Y, 4, kmul, ctypes.byref(E(1.0, 1.0, None, 0, 0)), None) == q.QGEMV_E_NULL
+    assert f(W, X, Y + 2, 4, kmul, ctypes.byref(E(1.0, 0.0, None, 0, q.QGEMV_F32)), None) == q.QGEMV_E_ALIGN
+    assert f(W, X, Y + 1, 4, kmul, ctypes.byref(E(1.0, 0.0, None, 0, q.QGEMV_F16)), None) == q.QGEMV_E_ALIGN
+    assert f(W, X, Y, 4, kmul, ctypes.byref(E(1.0, 2.0, C + 2, q.QGEMV_F32, 0)), None) == q.QGEMV_E_ALIGN
+    assert f(W, X, W + 32, 4, kmul, ctypes.byref(ok), None) == q.QGEMV_E_ALIAS
+    # c may be y itself only with the same element type
+    assert f(W, X, Y, 4, kmul, ctypes.byref(E(1.0, 1.0, Y + 4, q.QGEMV_F32, q.QGEMV_F32)), None) == q.QGEMV_E_ALIAS
+    assert f(W, X, Y, 4, kmul, ctypes.byref(E(1.0, 1.0, Y, q.QGEMV_F16, q.QGEMV_F32)), None) == q.QGEMV_E_ALIAS
+
+
+@pytest.mark.parametrize("name,kmul", [("qget_rows_q4k", 256), ("qget_rows_nvfp4", 32), ("qget_rows_tq1", 256)])
+def test_get_rows_validation(q, name, kmul):
+    f = getattr(q.lib(), name)
+    W, R, O = A, A + (1 << 32), A + (1 << 36)
+    assert f(W, 4, kmul, R, -1, O, 1, None) == q.QGEMV_E_SHAPE
+    assert f(W, 4, kmul, None, 5, O, 1, None) == q.QGEMV_E_SHAPE  # rows NULL: nrows <= M
+    assert f(W, 4, kmul // 2, R, 2, O, 1, None) == q.QGEMV_E_SHAPE
+    assert f(W, 4, kmul, R, 2, O, 3, None) == q.QGEMV_E_DTYPE
+    assert f(W, 4, kmul, R, 0, O, 1, None) == q.QGEMV_OK
+    assert f(W, 4, kmul, R, 2, None, 1, None) == q.QGEMV_E_NULL
+    assert f(None, 4, kmul, R, 2, O, 1, None) == q.QGEMV_E_NULL
+    assert f(W, 4, kmul, R, 2, O + 8, 1, None) == q.QGEMV_E_ALIGN
+    assert f(W, 4, kmul, R + 2, 2, O, 1, None) == q.QGEMV_E_ALIGN
+    assert f(W, 4, kmul, R, 2, W, 0, None) == q.QGEMV_E_ALIAS
+    assert f(W, 4, kmul, R, 2, R - 16, 0, None) == q.QGEMV_E_ALIAS
 
 
 @pytest.mark.parametrize("name,kmul", [("qdequant_q4k", 256), ("qdequant_nvfp4", 32), ("qdequant_tq1", 256)])
