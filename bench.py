@@ -11,7 +11,9 @@ the 256 MB Infinity Cache), so every launch streams its weights from HBM.
 Printed: ONE JSON line with the metric (achieved HBM GB/s of the kernel over
 the algorithmic bytes weights + x + y), the roofline object of the dominant
 kernel, the CPU baseline (the fp64 oracle on the host cores) and extra context
-(pure-read ceiling over the same bytes, the other formats' shapes).
+(pure-read ceiling over the same bytes, the other formats' shapes, the dense
+bf16 GEMV of the same shape, the general output stage, row materialisation and
+a Llama-8B per-token sweep).
 """
 from __future__ import annotations
 
@@ -32,9 +34,13 @@ EXTRA = [
     ("q4k", 4096, 4096, "Q4_K GEMV M=1, N=4096 x K=4096"),
     ("nvfp4", 4096, 14336, "NVFP4 W4A16 GEMV M=1, N=4096 x K=14336"),
     ("tq1", 14336, 4096, "TQ1_0 GEMV M=1, N=14336 x K=4096"),
+    ("bf16", 4096, 14336, "dense bf16 GEMV M=1, N=4096 x K=14336 (the Mojo fp4_gemv page's comparison)"),
 ]
 CASE_SEED = {("q4k", 4096, 4096): 0, ("q4k", 14336, 4096): 1, ("q4k", 4096, 14336): 1,
-             ("nvfp4", 4096, 14336): 2, ("tq1", 14336, 4096): 3}
+             ("nvfp4", 4096, 14336): 2, ("tq1", 14336, 4096): 3, ("bf16", 4096, 14336): 4}
+# The Mojo fp4_gemv page reports its NVFP4 GEMV 1.53x faster than a bf16 GEMV
+# at N = 4096, K = 14336 on an Apple M5 Max (context, not a target).
+PAGE_FP4_VS_BF16 = 1.53
 
 
 def algorithmic_bytes(fmt: str, n: int, k: int) -> int:
@@ -256,6 +262,121 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
     return res
 
 
+def time_graph(launch, count, steps, warmup, stream):
+    """Average microseconds of one of `count` distinct launches (launch(i, h)
+    enqueues number i on stream handle h), captured together in one HIP graph
+    and replayed; every copy first touched once, eagerly."""
+    import torch
+
+    h = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        for i in range(count):
+            launch(i, h)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(count):
+            launch(i, h)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup // count)):
+            g.replay()
+    reps = max(1, steps // count)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * ev0.elapsed_time(ev1) / (reps * count)
+    del g
+    return us
+
+
+def measure_epilogue(steps, warmup, rotate):
+    """The main Q4_K shape through the general output stage: fp16 y updated in
+    place, y = v + 0.5 y (a residual-style accumulate), against the plain call."""
+    import numpy as np
+    import torch
+
+    from dequant_gemv_amd import qgemv, synth
+
+    fmt, n, k, _ = MAIN
+    dev = torch.device("cuda:0")
+    seed = CASE_SEED[(fmt, n, k)]
+    w0 = torch.from_numpy(synth.weights(fmt, n, k, synth.W_SEED + seed)).to(dev)
+    ws = [w0] + [w0.clone() for _ in range(rotate - 1)]
+    x = torch.from_numpy(synth.activations(fmt, k, synth.X_SEED + seed).view(np.int16).copy()).to(dev)
+    y16 = torch.zeros(n, dtype=torch.float16, device=dev)
+    y32 = torch.empty(n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    us_ex = time_graph(lambda i, h: qgemv.qgemv_q4k_ex(ws[i], x, y16, n, k, 1.0, 0.5, y16, h),
+                       rotate, steps, warmup, stream)
+    us_plain = time_graph(lambda i, h: qgemv.qgemv_q4k(ws[i], x, y32, n, k, h), rotate, steps, warmup, stream)
+    del ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"Q4_K GEMV M=1, N={n} x K={k}, y (fp16) = x.W^T + 0.5 y in place",
+        "us_per_gemv": round(us_ex, 3),
+        "us_per_gemv_plain_fp32": round(us_plain, 3),
+        "overhead_us": round(us_ex - us_plain, 3),
+    }
+
+
+ROWS_CASES = [
+    # (format, rows of W, K, gathered rows or None for all, output type, description)
+    ("q4k", 4096, 14336, None, "f16", "Q4_K 4096 x 14336 materialised to fp16"),
+    ("nvfp4", 4096, 14336, None, "bf16", "NVFP4 4096 x 14336 materialised to bf16"),
+    ("tq1", 14336, 4096, None, "f16", "TQ1_0 14336 x 4096 materialised to fp16"),
+    ("q4k", 128256, 4096, 512, "f16", "Q4_K 128256 x 4096 table, 512 random rows to fp16 (prefill embedding lookup)"),
+]
+
+
+def measure_rows(steps, warmup, rotate):
+    """Row materialisation throughput: HBM bytes = packed bytes read + outputs
+    written (+ the int32 indices) per call."""
+    import numpy as np
+    import torch
+
+    from dequant_gemv_amd import qgemv, synth
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for fmt, n, k, nsel, dtype, desc in ROWS_CASES:
+        w0 = torch.from_numpy(synth.weights(fmt, n, k, 4100)).to(dev)
+        copies = max(1, min(rotate, (1 << 30) // w0.numel())) if nsel is None else 1
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        rows = None
+        nrows = n
+        if nsel is not None:
+            rows = torch.from_numpy(np.random.default_rng(4101).integers(0, n, nsel).astype(np.int32)).to(dev)
+            nrows = nsel
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+        o = torch.empty((nrows, k), dtype=tdt, device=dev)
+        # outputs rotate too (all-rows cases), so no call rewrites lines another left in the cache
+        ocount = max(1, min(copies, (1 << 30) // (o.numel() * o.element_size())))
+        os_ = [o] + [torch.empty_like(o) for _ in range(ocount - 1)]
+        fn = qgemv.GET_ROWS[fmt]
+        stream = torch.cuda.Stream()
+        us = time_graph(lambda i, h: fn(ws[i % copies], n, k, rows, nrows, os_[i % ocount], h), max(copies, 8),
+                        max(64, steps // 8), max(64, warmup // 8), stream)
+        per_row = synth.weight_bytes(fmt, 1, k)
+        nbytes = nrows * per_row + nrows * k * o.element_size() + (4 * nrows if rows is not None else 0)
+        out[f"{fmt}_{n}x{k}_{nsel or 'all'}_{dtype}"] = {
+            "workload": desc,
+            "us_per_call": round(us, 3),
+            "bytes_per_call": nbytes,
+            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+        }
+        log(f"[bench] rows {desc}: {us:.3f} us, {out[list(out)[-1]]['gbps']} GB/s")
+        del ws, o, os_
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(fmt, n, k, budget_s=10.0):
     """The fp64 oracle as it stands, all host cores, on the same workload."""
     import numpy as np
@@ -302,7 +423,7 @@ def main():
     ap.add_argument("--sweep", default="mixed",
                     help="Llama-8B per-token sweep(s) to time among mixed,q4k,nvfp4,tq1 (comma list; 'none' to skip)")
     ap.add_argument("--sweep-tokens", type=int, default=20)
-    ap.add_argument("--fmt", default=None, help="measure only this format (q4k, nvfp4, tq1) at N,K")
+    ap.add_argument("--fmt", default=None, help="measure only this format (q4k, nvfp4, tq1, f16, bf16) at N,K")
     ap.add_argument("--n", type=int, default=None)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 64 MiB device copy (a known-size reference for the HBM byte counters)")
@@ -354,6 +475,21 @@ def main():
             }
             log(f"[bench] {efmt} {en}x{ek}: {r['us_per_launch_event']:.3f} us, {r['gbps_event']:.1f} GB/s")
 
+    fp4_vs_bf16 = None
+    if "nvfp4_4096x14336" in extra and "bf16_4096x14336" in extra:
+        fp4_vs_bf16 = {
+            "speedup": round(extra["bf16_4096x14336"]["us_per_gemv"] / extra["nvfp4_4096x14336"]["us_per_gemv"], 3),
+            "bytes_ratio": round(algorithmic_bytes("bf16", 4096, 14336) / algorithmic_bytes("nvfp4", 4096, 14336), 3),
+            "page_speedup_apple_m5_max": PAGE_FP4_VS_BF16,
+        }
+        log(f"[bench] NVFP4 vs bf16 at 4096x14336: {fp4_vs_bf16['speedup']}x")
+
+    epilogue = rows_res = None
+    if not args.no_extra and not args.fmt:
+        epilogue = measure_epilogue(max(args.rotate, args.steps // 4), args.warmup, args.rotate)
+        log(f"[bench] epilogue: {epilogue['us_per_gemv']} us (plain {epilogue['us_per_gemv_plain_fp32']} us)")
+        rows_res = measure_rows(args.steps, args.warmup, args.rotate)
+
     sweeps = {}
     if not args.no_extra and not args.fmt and args.sweep != "none":
         for mix in args.sweep.split(","):
@@ -402,6 +538,9 @@ def main():
                          "note": "pure dwordx4 read of the same weight bytes, same rotation"},
         "cpu_baseline": cpu,
         "other_shapes": extra,
+        "fp4_vs_bf16": fp4_vs_bf16,
+        "epilogue": epilogue,
+        "get_rows": rows_res,
         "decode_sweep": sweeps,
         "build_id": have,
         "gpu": torch.cuda.get_device_name(0),
