@@ -115,8 +115,8 @@ int get_rows(Fmt f, const void* w, int64_t m, int64_t k, const int32_t* rows, in
   if (nrows < 0 || nrows > kMaxM || (!rows && nrows > m)) return QGEMV_E_SHAPE;
   if (!valid_dtype(dtype)) return QGEMV_E_DTYPE;
   if (nrows == 0) return QGEMV_OK;
-  // tasks of 32 (Q4_K, NVFP4) or 16 (TQ1_0) weights in workgroups of up to 256
-  const int64_t tasks = f == kTq1 ? k / 16 : k / 32;
+  // tasks of 16 output bytes each, in workgroups of up to 256
+  const int64_t tasks = k * dtype_size(dtype) / 16;
   const int64_t per_wg = tasks < 256 ? tasks : 256;
   if (nrows * ((tasks + per_wg - 1) / per_wg) > kMaxM) return QGEMV_E_SHAPE;
   if ((m > 0 && !w) || !out) return QGEMV_E_NULL;

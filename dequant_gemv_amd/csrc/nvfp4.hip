@@ -209,41 +209,52 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
   store_rows<R>(acc, out, row0, nrows, 1.f, lane);
 }
 
-// Row materialisation.  One thread per (output row, 16 nibble bytes) = 32
-// weights = two scale blocks; every weight e2m1 * |scale| is exact in fp32
-// (and in fp16 / bf16).
-template <typename T>
+// Row materialisation.  Task t of an output row makes weights
+// [E t, E t + E) (E = 8 or 4): E/2 nibble bytes and the one scale byte of
+// their 16-weight block; every weight e2m1 * |scale| is exact in fp32 (and in
+// fp16 / bf16).
+#ifndef QGEMV_NVFP4_ROWS_U
+#define QGEMV_NVFP4_ROWS_U 2  // row-materialisation tasks per thread
+#endif
+
+struct Nvfp4RowIn {
+  unsigned q;
+  unsigned sc;
+};
+
+template <typename T, int U>
 __global__ __launch_bounds__(256) void nvfp4_rows_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                          const int32_t* __restrict__ rows, T* __restrict__ out,
                                                          int bpr) {
+  constexpr int E = kRowsE<T>;
   const int j = blockIdx.x / bpr;
-  const int t = (blockIdx.x - j * bpr) * blockDim.x + threadIdx.x;
-  if (t >= k / 32) return;
-  T* const o = out + (int64_t)j * k + 32 * t;
   const int r = source_row(rows, j, n);
-  if (r < 0) {
-    store16_nan(o);
-    store16_nan(o + 16);
-    return;
-  }
-  const u32x4 v = *reinterpret_cast<const u32x4*>(w + (int64_t)r * (k / 2) + 16 * t);
-  const unsigned sc =
-      *reinterpret_cast<const uint16_t*>(w + (int64_t)n * (k / 2) + (int64_t)r * (k / 16) + 2 * t);
-  const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 0));
-  const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)sc, 1));
-  const unsigned q[4] = {v.x, v.y, v.z, v.w};
-  float a[16], b[16];
+  const int64_t rr = r < 0 ? 0 : r;
+  const uint8_t* const nib = w + rr * (k / 2);
+  const uint8_t* const scl = w + (int64_t)n * (k / 2) + rr * (k / 16);
+  T* const orow = out + (int64_t)j * k;
+  rows_thread<U, Nvfp4RowIn>(
+      bpr, k / E, r >= 0,
+      [&](int t) {
+        const int e0 = t * E;
+        Nvfp4RowIn in;
+        in.q = E == 8 ? *reinterpret_cast<const uint32_t*>(nib + e0 / 2)
+                      : *reinterpret_cast<const uint16_t*>(nib + e0 / 2);
+        in.sc = scl[e0 / 16];
+        return in;
+      },
+      [&](int t, const Nvfp4RowIn& in) {
+        const float s = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)in.sc, 0));
+        float v[E];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const f32x2 e = fp4x2_f32(q[i >> 2], i);
-    a[2 * i] = e.x * s0;
-    a[2 * i + 1] = e.y * s0;
-    const f32x2 f = fp4x2_f32(q[(i + 8) >> 2], i + 8);
-    b[2 * i] = f.x * s1;
-    b[2 * i + 1] = f.y * s1;
-  }
-  store16(o, a);
-  store16(o + 16, b);
+        for (int i = 0; i < E / 2; ++i) {
+          const f32x2 p = fp4x2_f32(in.q, i);
+          v[2 * i] = p.x * s;
+          v[2 * i + 1] = p.y * s;
+        }
+        store_e(orow + t * E, v);
+      },
+      [&](int t) { store_e_nan(orow + t * E); });
 }
 
 template <int R, typename Out>
@@ -308,13 +319,22 @@ hipError_t launch_nvfp4_gemv(const void* w, const void* x, const OutEx& y, int64
   return launch_nvfp4_gemv_out(w, x, y, n, k, s);
 }
 
+template <typename T, int U>
+static hipError_t launch_nvfp4_rows_u(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
+                                    void* out, hipStream_t s) {
+  const RowsGeom g = rows_geom(k / kRowsE<T>, nrows, U);
+  hipLaunchKernelGGL((nvfp4_rows_kernel<T, U>), dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w,
+                     (int)n, (int)k, rows, (T*)out, g.bpr);
+  return hipGetLastError();
+}
+
+// Small launches (a few hundred gathered rows) take one task per thread so
+// that they still spread over the whole chip.
 template <typename T>
 static hipError_t launch_nvfp4_rows_t(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
-                                      void* out, hipStream_t s) {
-  const RowsGeom g = rows_geom(k / 32, nrows);
-  hipLaunchKernelGGL(nvfp4_rows_kernel<T>, dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w, (int)n,
-                     (int)k, rows, (T*)out, g.bpr);
-  return hipGetLastError();
+                                    void* out, hipStream_t s) {
+  if (nrows * (k / kRowsE<T>) < kRowsSmallTasks) return launch_nvfp4_rows_u<T, 1>(w, n, k, rows, nrows, out, s);
+  return launch_nvfp4_rows_u<T, QGEMV_NVFP4_ROWS_U>(w, n, k, rows, nrows, out, s);
 }
 
 hipError_t launch_nvfp4_get_rows(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,

@@ -341,42 +341,60 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
   store_rows<R>(acc, out, row0, nrows, 0x1p24f, lane);
 }
 
-// Row materialisation.  One thread per (output row, block, 16-byte nibble
-// slice): 32 weights, each the correctly rounded fp32 of d*s*q - dmin*m (both
-// products are exact in fp32, so one fma rounds once), then converted to T.
-template <typename T>
+// Row materialisation.  Task t of an output row makes weights
+// [E t, E t + E) (E = 8 or 4, all in one 32-weight group g of block b): the
+// block header (d, dmin, packed scales) and E nibbles, low or high, of
+// qs[32 c + l .. + E) with c = g / 2.  Each weight is the correctly rounded
+// fp32 of d*s*q - dmin*m (both products are exact in fp32, so one fma rounds
+// once), then converted to T.
+#ifndef QGEMV_Q4K_ROWS_U
+#define QGEMV_Q4K_ROWS_U 8  // row-materialisation tasks per thread
+#endif
+
+struct Q4kRowIn {
+  u32x4 hdr;
+  uint64_t q;
+};
+
+template <typename T, int U>
 __global__ __launch_bounds__(256) void q4k_rows_kernel(const uint8_t* __restrict__ w, int n, int nb,
                                                        const int32_t* __restrict__ rows, T* __restrict__ out,
                                                        int bpr) {
+  constexpr int E = kRowsE<T>;
   const int j = blockIdx.x / bpr;
-  const int t = (blockIdx.x - j * bpr) * blockDim.x + threadIdx.x;
-  if (t >= nb * 8) return;
-  const int b = t >> 3, p = t & 7, c = p >> 1, h = p & 1;
-  T* const o = out + ((int64_t)j * nb + b) * 256 + 64 * c + 16 * h;
   const int r = source_row(rows, j, n);
-  if (r < 0) {
-    store16_nan(o);
-    store16_nan(o + 32);
-    return;
-  }
-  const uint8_t* const blk = w + ((int64_t)r * nb + b) * kQ4kBytes;
-  const u32x4 hdr = *reinterpret_cast<const u32x4*>(blk);
-  const u32x4 qv = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * p);
-  const Q4kScaleSel sel(c);
-  const unsigned sp = sel.scales(hdr.y, hdr.w), mp = sel.mins(hdr.z, hdr.w);
-  const float d = f16lo(hdr.x), dmin = f16hi(hdr.x);
-  const float dsa = d * (float)(sp & 0xFFu), dsb = d * (float)((sp >> 8) & 0xFFu);
-  const float dma = dmin * (float)(mp & 0xFFu), dmb = dmin * (float)((mp >> 8) & 0xFFu);
-  const unsigned q[4] = {qv.x, qv.y, qv.z, qv.w};
-  float lo[16], hi[16];
+  const uint8_t* const wr = w + (int64_t)(r < 0 ? 0 : r) * nb * kQ4kBytes;
+  T* const orow = out + (int64_t)j * nb * 256;
+  rows_thread<U, Q4kRowIn>(
+      bpr, nb * (256 / E), r >= 0,
+      [&](int t) {
+        const int e0 = t * E, e = e0 & 255;
+        const uint8_t* const blk = wr + (e0 >> 8) * kQ4kBytes;
+        Q4kRowIn in;
+        in.hdr = *reinterpret_cast<const u32x4*>(blk);
+        const uint8_t* const qp = blk + 16 + 32 * (e >> 6) + (e & 31);
+        if constexpr (E == 8)
+          in.q = *reinterpret_cast<const uint64_t*>(qp);
+        else
+          in.q = *reinterpret_cast<const uint32_t*>(qp);
+        return in;
+      },
+      [&](int t, const Q4kRowIn& in) {
+        const int e = (t * E) & 255;
+        const int c = e >> 6, hi = (e >> 5) & 1;
+        const Q4kScaleSel sel(c);
+        const unsigned sh = 8u * (unsigned)hi;
+        const unsigned sg = (sel.scales(in.hdr.y, in.hdr.w) >> sh) & 0xFFu;
+        const unsigned mg = (sel.mins(in.hdr.z, in.hdr.w) >> sh) & 0xFFu;
+        const float ds = f16lo(in.hdr.x) * (float)sg, dm = f16hi(in.hdr.x) * (float)mg;
+        const unsigned nsh = 4u * (unsigned)hi;
+        float v[E];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const unsigned byte = (q[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-    lo[i] = __builtin_fmaf(dsa, (float)(byte & 15u), -dma);
-    hi[i] = __builtin_fmaf(dsb, (float)(byte >> 4), -dmb);
-  }
-  store16(o, lo);
-  store16(o + 32, hi);
+        for (int i = 0; i < E; ++i)
+          v[i] = __builtin_fmaf(ds, (float)((unsigned)(in.q >> (8 * i + nsh)) & 15u), -dm);
+        store_e(orow + t * E, v);
+      },
+      [&](int t) { store_e_nan(orow + t * E); });
 }
 
 template <typename Out>
@@ -457,13 +475,22 @@ hipError_t launch_q4k_gemv(const void* w, const void* x, const OutEx& y, int64_t
   return launch_q4k_gemv_out(w, x, y, n, k, s);
 }
 
+template <typename T, int U>
+static hipError_t launch_q4k_rows_u(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
+                                    void* out, hipStream_t s) {
+  const RowsGeom g = rows_geom(k / kRowsE<T>, nrows, U);
+  hipLaunchKernelGGL((q4k_rows_kernel<T, U>), dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w,
+                     (int)n, (int)(k / 256), rows, (T*)out, g.bpr);
+  return hipGetLastError();
+}
+
+// Small launches (a few hundred gathered rows) take one task per thread so
+// that they still spread over the whole chip.
 template <typename T>
 static hipError_t launch_q4k_rows_t(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
                                     void* out, hipStream_t s) {
-  const RowsGeom g = rows_geom(k / 256 * 8, nrows);
-  hipLaunchKernelGGL(q4k_rows_kernel<T>, dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w, (int)n,
-                     (int)(k / 256), rows, (T*)out, g.bpr);
-  return hipGetLastError();
+  if (nrows * (k / kRowsE<T>) < kRowsSmallTasks) return launch_q4k_rows_u<T, 1>(w, n, k, rows, nrows, out, s);
+  return launch_q4k_rows_u<T, QGEMV_Q4K_ROWS_U>(w, n, k, rows, nrows, out, s);
 }
 
 hipError_t launch_q4k_get_rows(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows, void* out,

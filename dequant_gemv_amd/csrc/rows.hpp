@@ -1,11 +1,17 @@
 // Shared pieces of the row-materialisation (GET_ROWS) kernels: output element
-// conversion, 16-element vector stores and the launch geometry.
+// conversion, vector stores and the launch geometry.
 //
-// Every format's kernel splits an output row into tasks of 16 or 32 weights
-// that read one small contiguous piece of the packed row (a 16-byte nibble
-// slice, a 16-element run of a ternary block) and write their outputs with
-// 16-byte stores.  Workgroup b covers tasks [(b % bpr) * B, ...) of output
-// row b / bpr, so no thread ever divides by a runtime value.
+// Every format's kernel gives each thread 16 bytes of output: E = 8 weights
+// for fp16 / bf16, 4 for fp32, consecutive in the row.  Consecutive threads
+// own consecutive 16-byte pieces, so each wave-wide store writes one
+// contiguous KiB; the packed bytes a thread needs are a few bytes of one
+// block (plus its header), read with small loads that neighbouring lanes
+// share.  A thread owns U such tasks, B apart (B = threads per workgroup), and
+// issues the loads of all U before converting and storing any, so a wave keeps
+// U times more bytes in flight than one task would (a single load-convert-store
+// per thread leaves the kernel bound by load latency).  Workgroup b covers
+// tasks [(b % bpr) * B * U, ...) of output row b / bpr, so no thread divides
+// by a runtime value.
 #pragma once
 #include "device.hpp"
 #include "epilogue.hpp"
@@ -22,30 +28,41 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
   }
 }
 
-// out[0..16) = v converted to T, with 16-byte stores (dst 16-byte aligned for
-// fp32, 32-byte for 16-bit types: both hold for every task of these kernels).
+// Outputs per thread (16 bytes of T).
 template <typename T>
-__device__ __forceinline__ void store16(T* dst, const float (&v)[16]) {
+constexpr int kRowsE = 16 / (int)sizeof(T);
+
+// dst[0..E) = v converted to T, one 16-byte store (dst 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ void store_e(T* dst, const float (&v)[kRowsE<T>]) {
   if constexpr (sizeof(T) == 4) {
-#pragma unroll
-    for (int i = 0; i < 16; i += 4)
-      *reinterpret_cast<float4*>(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
-#pragma unroll
-    for (int i = 0; i < 16; i += 8)
-      *reinterpret_cast<u32x4*>(dst + i) = u32x4{pack2<T>(v[i], v[i + 1]), pack2<T>(v[i + 2], v[i + 3]),
-                                                 pack2<T>(v[i + 4], v[i + 5]), pack2<T>(v[i + 6], v[i + 7])};
+    *reinterpret_cast<u32x4*>(dst) = u32x4{pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]), pack2<T>(v[4], v[5]),
+                                           pack2<T>(v[6], v[7])};
   }
 }
 
-// 16 quiet NaNs (clear sign bit) of the output type: the row of an index
-// outside [0, n).
+// E quiet NaNs (clear sign bit) of the output type: the piece of a row whose
+// index is outside [0, n).
 template <typename T>
-__device__ __forceinline__ void store16_nan(T* dst) {
+__device__ __forceinline__ void store_e_nan(T* dst) {
   const unsigned q = sizeof(T) == 4 ? 0x7FC00000u : (__is_same(T, _Float16) ? 0x7E007E00u : 0x7FC07FC0u);
-  const u32x4 v = {q, q, q, q};
+  *reinterpret_cast<u32x4*>(dst) = u32x4{q, q, q, q};
+}
+
+// Little-endian value of BYTES (2, 4 or 8) bytes at an even byte offset of a
+// buffer, read as separate 16-bit buffer loads.  The ternary blocks are 54
+// bytes, so their fields are only 2-byte aligned; plain 16-bit pointer loads
+// would be merged by the compiler into dword / dwordx2 loads at addresses
+// that are not 4-byte aligned, and those do not reliably return the bytes
+// asked for.  Buffer-load intrinsics are never merged.
+template <int BYTES>
+__device__ __forceinline__ uint64_t load_le_a2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  uint64_t v = 0;
 #pragma unroll
-  for (int i = 0; i < 16; i += 16 / (int)sizeof(T)) *reinterpret_cast<u32x4*>(dst + i) = v;
+  for (int i = 0; i < BYTES / 2; ++i) v |= (uint64_t)ld16(r, off + 2u * (uint32_t)i) << (16 * i);
+  return v;
 }
 
 // Source row of output row j, or -1 when the index is outside [0, n).
@@ -54,20 +71,50 @@ __device__ __forceinline__ int source_row(const int32_t* rows, int j, int n) {
   return (unsigned)r < (unsigned)n ? r : -1;
 }
 
+// Below this many tasks in a launch the kernels run one task per thread.
+constexpr int64_t kRowsSmallTasks = int64_t(1) << 21;
+
 struct RowsGeom {
   int block;  // threads per workgroup
   int bpr;    // workgroups per output row
   int64_t grid;
 };
 
-// Tasks per row -> workgroup size (a multiple of 64, at most 256) and count.
-inline RowsGeom rows_geom(int64_t tasks, int64_t nrows_out) {
+// Tasks per row and per thread (U) -> workgroup size (a multiple of 64, at
+// most 256) and count.
+inline RowsGeom rows_geom(int64_t tasks, int64_t nrows_out, int u) {
   RowsGeom g;
-  const int64_t b = tasks < 256 ? (tasks + 63) / 64 * 64 : 256;
+  const int64_t per_thread = (tasks + u - 1) / u;
+  const int64_t b = per_thread < 256 ? (per_thread + 63) / 64 * 64 : 256;
   g.block = (int)b;
-  g.bpr = (int)((tasks + b - 1) / b);
+  g.bpr = (int)((tasks + b * u - 1) / (b * u));
   g.grid = nrows_out * g.bpr;
   return g;
+}
+
+// Runs a row-materialisation thread owning U tasks: load(t) fetches what task
+// t needs, emit(t, in) converts and stores it, fill(t) stores task t's quiet
+// NaNs.
+template <int U, typename In, typename Load, typename Emit, typename Fill>
+__device__ __forceinline__ void rows_thread(int bpr, int tasks, bool valid, Load&& load, Emit&& emit, Fill&& fill) {
+  const int j = blockIdx.x / bpr;
+  const int t0 = (blockIdx.x - j * bpr) * blockDim.x * U + threadIdx.x;
+  In in[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = t0 + u * (int)blockDim.x;
+    if (valid && t < tasks) in[u] = load(t);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = t0 + u * (int)blockDim.x;
+    if (t < tasks) {
+      if (valid)
+        emit(t, in[u]);
+      else
+        fill(t);
+    }
+  }
 }
 
 }  // namespace qgemv

@@ -332,41 +332,101 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   store_rows<R>(acc, out, row0, nrows, 1.f, lane);
 }
 
-// Row materialisation.  One thread per (output row, block, run of 16
-// elements il): elements 16 il .. 16 il + 15.  For il < 10 they are digit il/2
-// of qs[16 (il%2) + e]; for il < 15 digit il-10 of qs[32 + e]; il = 15 is
-// digit e/4 of qh[e%4] (the section-2 element order of the TQ1_0 page).
-// Weight = d * (digit - 1), exact in fp32 (and in fp16).
-template <typename T>
+// Row materialisation.  Task t of an output row makes weights
+// [E t, E t + E) (E = 8 or 4) of block b, in the section-2 element order of
+// the TQ1_0 page: element 32 k + j (j < 32) is digit k of qs[j], element
+// 160 + 16 k + i (i < 16) digit k of qs[32 + i], element 240 + 4 k + m digit
+// k of qh[m].  So the E weights are one digit of E consecutive qs bytes, or
+// (past element 240) E/4 digits of the four qh bytes.  Weight = d * (digit -
+// 1), exact in fp32 (and in fp16).
+//
+// A weight can only be one of three values, d * -1, d * 0 and d * 1, so the
+// thread computes those three once (with the same fp32 arithmetic, then the
+// conversion to T) and each weight only selects one.  For 16-bit outputs two
+// weights are done at once: their bytes sit in the two 16-bit halves of a
+// register, packed 16-bit multiplies give digit = ((3^k * q) mod 256) * 3 >> 8
+// ("Not applicable" section of the TQ1_0 page) for both, and one v_perm_b32
+// picks each half's 2 output bytes out of the 6-byte table (-d, 0d, +d).
+__device__ __forceinline__ u16x2 tq1_digits2(u16x2 q, unsigned short p) {
+  const u16x2 m = (q * u16x2{p, p}) & u16x2{0xFF, 0xFF};
+  return (m * u16x2{3, 3}) >> u16x2{8, 8};
+}
+
+#ifndef QGEMV_TQ1_ROWS_U
+#define QGEMV_TQ1_ROWS_U 2  // row-materialisation tasks per thread
+#endif
+
+struct Tq1RowIn {
+  uint64_t bytes;
+  unsigned short d;
+};
+
+template <typename T, int U>
 __global__ __launch_bounds__(256) void tq1_rows_kernel(const uint8_t* __restrict__ w, int n, int nb,
                                                        const int32_t* __restrict__ rows, T* __restrict__ out,
                                                        int bpr) {
+  constexpr int E = kRowsE<T>;
   const int j = blockIdx.x / bpr;
-  const int t = (blockIdx.x - j * bpr) * blockDim.x + threadIdx.x;
-  if (t >= nb * 16) return;
-  const int blk_i = t >> 4, il = t & 15;
-  T* const o = out + ((int64_t)j * nb + blk_i) * 256 + 16 * il;
   const int r = source_row(rows, j, n);
-  if (r < 0) {
-    store16_nan(o);
-    return;
-  }
-  const uint8_t* const b = w + ((int64_t)r * nb + blk_i) * kTq1Bytes;
-  const float d = (float)__builtin_bit_cast(_Float16, (unsigned short)(b[52] | (b[53] << 8)));
-  float v[16];
+  // the row's bytes (the row is the same for the whole workgroup)
+  const auto wr = make_rsrc(w + (int64_t)(r < 0 ? 0 : r) * nb * kTq1Bytes, r < 0 ? 0u : (uint32_t)(nb * kTq1Bytes));
+  T* const orow = out + (int64_t)j * nb * 256;
+  // 3^k for k = 0..4 without branches: 1, 3, 9, 27 are the bytes of one word
+  auto pow3 = [](int k) -> unsigned short {
+    const unsigned lo = (0x1B090301u >> (8 * (k & 3))) & 0xFFu;
+    return (unsigned short)(k >= 4 ? 81u : lo);
+  };
+  rows_thread<U, Tq1RowIn>(
+      bpr, nb * (256 / E), r >= 0,
+      [&](int t) {
+        const int e0 = t * E, e = e0 & 255;
+        const uint32_t blk = (uint32_t)((e0 >> 8) * kTq1Bytes);
+        // the run's qs bytes, or the qh dword (and the bytes after it, unused);
+        // every lane issues the same loads, with no branch around them
+        const uint32_t off = e < 160 ? (e & 31) : (e >= 240 ? 48 : 32 + ((e - 160) & 15));
+        Tq1RowIn in;
+        in.bytes = load_le_a2<E>(wr, blk + off);
+        in.d = ld16(wr, blk + 52);
+        return in;
+      },
+      [&](int t, const Tq1RowIn& in) {
+        const int e = (t * E) & 255;
+        const bool qh = e >= 240;
+        const int k0 = e < 160 ? (e >> 5) : (qh ? (e - 240) >> 2 : (e - 160) >> 4);
+        const float d = (float)__builtin_bit_cast(_Float16, in.d);
+        if constexpr (E == 8) {
+          // the three possible outputs as 16-bit codes: table bytes 0-1, 2-3, 4-5
+          const unsigned vm = pack2<T>(d * -1.f, d * 0.f);
+          const unsigned vp = pack2<T>(d * 1.f, 0.f);
+          unsigned res[4];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    int byte, k;
-    if (il < 10) { byte = 16 * (il & 1) + e; k = il >> 1; }
-    else if (il < 15) { byte = 32 + e; k = il - 10; }
-    else { byte = 48 + (e & 3); k = e >> 2; }
-    int p = 1;
-    for (int i = 0; i < k; ++i) p *= 3;
-    const int q = b[byte];
-    const int digit = (p * 3 * q) / 256 - 3 * ((p * q) / 256);
-    v[e] = d * (float)(digit - 1);
-  }
-  store16(o, v);
+          for (int pr = 0; pr < 4; ++pr) {
+            // elements 2pr, 2pr+1: bytes (2pr, 2pr+1) of the run, or of the qh dword
+            const int b0 = qh ? (2 * pr) & 3 : 2 * pr;
+            const unsigned short p = pow3(qh ? k0 + (pr >> 1) : k0);
+            const unsigned word = (unsigned)(in.bytes >> (8 * (b0 & 4)));
+            const unsigned pair =
+                __builtin_amdgcn_perm(0u, word, 0x0C000C00u | (unsigned)(b0 & 3) | ((unsigned)((b0 & 3) + 1) << 16));
+            const u16x2 dg = tq1_digits2(__builtin_bit_cast(u16x2, pair), p);
+            const u16x2 sel = dg * u16x2{0x0202, 0x0202} + u16x2{0x0100, 0x0100};
+            res[pr] = __builtin_amdgcn_perm(vp, vm, __builtin_bit_cast(unsigned, sel));
+          }
+          *reinterpret_cast<u32x4*>(orow + t * E) = u32x4{res[0], res[1], res[2], res[3]};
+        } else {
+          const float vals[3] = {d * -1.f, d * 0.f, d * 1.f};
+          float v[E];
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            const int bi = qh ? (i & 3) : i;
+            const unsigned q = (unsigned)(in.bytes >> (8 * bi)) & 0xFFu;
+            const unsigned pq = (pow3(qh ? k0 + (i >> 2) : k0) * q) & 0xFFu;
+            const unsigned digit = (3u * pq) >> 8;
+            v[i] = digit == 0 ? vals[0] : digit == 1 ? vals[1] : vals[2];
+          }
+          store_e(orow + t * E, v);
+        }
+      },
+      [&](int t) { store_e_nan(orow + t * E); });
 }
 
 template <int R, typename Out>
@@ -423,13 +483,22 @@ hipError_t launch_tq1_gemv(const void* w, const void* x, const OutEx& y, int64_t
   return launch_tq1_gemv_out(w, x, y, n, k, s);
 }
 
+template <typename T, int U>
+static hipError_t launch_tq1_rows_u(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
+                                    void* out, hipStream_t s) {
+  const RowsGeom g = rows_geom(k / kRowsE<T>, nrows, U);
+  hipLaunchKernelGGL((tq1_rows_kernel<T, U>), dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w,
+                     (int)n, (int)(k / 256), rows, (T*)out, g.bpr);
+  return hipGetLastError();
+}
+
+// Small launches (a few hundred gathered rows) take one task per thread so
+// that they still spread over the whole chip.
 template <typename T>
 static hipError_t launch_tq1_rows_t(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows,
                                     void* out, hipStream_t s) {
-  const RowsGeom g = rows_geom(k / 256 * 16, nrows);
-  hipLaunchKernelGGL(tq1_rows_kernel<T>, dim3((unsigned)g.grid), dim3(g.block), 0, s, (const uint8_t*)w, (int)n,
-                     (int)(k / 256), rows, (T*)out, g.bpr);
-  return hipGetLastError();
+  if (nrows * (k / kRowsE<T>) < kRowsSmallTasks) return launch_tq1_rows_u<T, 1>(w, n, k, rows, nrows, out, s);
+  return launch_tq1_rows_u<T, QGEMV_TQ1_ROWS_U>(w, n, k, rows, nrows, out, s);
 }
 
 hipError_t launch_tq1_get_rows(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows, void* out,
