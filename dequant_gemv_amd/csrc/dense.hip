@@ -69,11 +69,16 @@ __global__ __launch_bounds__(64 * W) void dense_gemv_kernel(const uint8_t* __res
   const int tail = row_bytes - ((kc - 1) << 10);
   const bool tail_lane = 16 * lane < tail;
 
+  // the output stage's input for the first row (a row's is fetched when the
+  // previous row ends, a whole row of loads ahead of its use)
+  auto pre = out.prefetch(row0, 0, nrows > 0);
+
   // Activation copy straight into LDS: piece P (1 KiB) by wave P % W; bytes
   // past 2K read as zero.
   const auto xr = make_rsrc(x, (uint32_t)row_bytes);
   for (int piece = wave; piece < kc; piece += W)
     ld128_lds(xr, xs + piece * 1024, (uint32_t)(piece * 1024 + 16 * lane));
+  compiler_fence();
 
   // First DEPTH weight loads of the wave's run.  Loads are never skipped:
   // past the end of the run their offsets fall outside the descriptor and
@@ -110,10 +115,11 @@ __global__ __launch_bounds__(64 * W) void dense_gemv_kernel(const uint8_t* __res
       buf[i] = ld128w(wr, next_off());
       if (++c == kc) {  // row j done (units past the run belong to rows >= nrows)
         float a[1] = {acc};
-        store_rows<1>(a, out, row0 + j, j < nrows ? 1 : 0, 1.f, lane);
+        store_rows<1>(a, out, pre, row0 + j, j < nrows ? 1 : 0, 1.f, lane);
         acc = 0.f;
         c = 0;
         ++j;
+        pre = out.prefetch(row0, j, j < nrows);
       }
     }
   }

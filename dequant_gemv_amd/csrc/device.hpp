@@ -151,10 +151,19 @@ __device__ __forceinline__ void wave_reduce_rows(float (&v)[R]) {
 
 // s_waitcnt vmcnt(N) for a compile-time 0 <= N <= 63 (gfx9 encoding: vmcnt
 // bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima, i.e. no wait).
+// Compiler-only memory fence (emits nothing): no load, store or LDS access
+// is moved across it.  The kernels count their own loads for the vmcnt
+// waits, which is only sound if loads are issued, and waits placed, exactly
+// in source order; the compiler otherwise treats independent buffer loads
+// (and loads around a wait) as free to reorder.
+__device__ __forceinline__ void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  compiler_fence();
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  compiler_fence();
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;

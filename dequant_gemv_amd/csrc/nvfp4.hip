@@ -160,12 +160,16 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
   const auto sr = make_rsrc(w + (int64_t)n * kNibRow + (int64_t)row0 * kScRow, sc_len);
   stream_loads<0, C::kScLoads, QGEMV_WLOAD_AUX>(sr, sc_stage, lane);
   const unsigned short sc_tail = ld16(sr, tail_lane ? sc_full + 2u * lane : sc_len);
+  compiler_fence();  // counted by the wait below: stays between the scale and nibble loads
   const auto nr = make_rsrc(w + (int64_t)row0 * kNibRow, (uint32_t)(nrows * kNibRow));
   stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
 
   wait_vm<S::kUpFront>();  // activations, scales and the scale tail (issued first) are in
   if (tail_lane) *reinterpret_cast<unsigned short*>(sc_stage + sc_full + 2 * lane) = sc_tail;
   __builtin_amdgcn_s_barrier();  // ... every wave's activation pieces too
+  // the output stage's input for the wave's rows, after the barrier's wait
+  // (the stream's later waits only get stricter by this one load)
+  const auto pre = prefetch_rows(out, row0, nrows, lane);
   stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX>(nr, nib_stage, lane);
 
   unsigned X[KC][16];
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
     }
     acc[r] = __builtin_fmaf(s1, a1, __builtin_fmaf(s0, a0, acc[r]));
   });
-  store_rows<R>(acc, out, row0, nrows, 1.f, lane);
+  store_rows<R>(acc, out, pre, row0, nrows, 1.f, lane);
 }
 
 // Row materialisation.  Task t of an output row makes weights

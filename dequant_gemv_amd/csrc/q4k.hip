@@ -265,6 +265,9 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
 
   wait_vm<S::issued_before(0)>();  // this wave's activation pieces (issued before the weights) are in LDS
   __builtin_amdgcn_s_barrier();  // ... and every other wave's
+  // the output stage's input for the wave's rows, after the barrier's wait
+  // (the stream's later waits only get stricter by this one load)
+  const auto pre = prefetch_rows(out, row0, nrows, lane);
 
   // The lane's activations for every chunk, as fp16 pairs matching the masked
   // nibble layout, and their group sums (times 2^-24, see the K-split kernel).
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
     else
       acc[r] += part;
   });
-  store_rows<R>(acc, out, row0, nrows, 0x1p24f, lane);
+  store_rows<R>(acc, out, pre, row0, nrows, 0x1p24f, lane);
 }
 
 // Row materialisation.  Task t of an output row makes weights

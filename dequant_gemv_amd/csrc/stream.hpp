@@ -39,12 +39,16 @@ struct StreamSchedule {
 };
 
 // Issue loads [B, E) of a stream whose LDS stage starts at `stage`.
+// The group stays between the memory accesses before and after it (the
+// counted waits depend on the issue order of groups).
 template <int B, int E, int AUX>
 __device__ __forceinline__ void stream_loads(__amdgpu_buffer_rsrc_t r, unsigned char* stage, int lane) {
+  compiler_fence();
   static_for<B, E>([&](auto i) {
     constexpr int I = decltype(i)::value;
     ld128_lds<AUX>(r, stage + I * 1024, (uint32_t)(I * 1024 + 16 * lane));
   });
+  compiler_fence();
 }
 
 // The workgroup's copy of the activations: PIECES one-KiB pieces dealt to the
@@ -55,25 +59,40 @@ template <int PIECES, int W, typename SrcFn>
 __device__ __forceinline__ void load_shared_pieces(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int wave, int lane,
                                                    SrcFn src) {
   constexpr int kPer = (PIECES + W - 1) / W;
+  compiler_fence();
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int piece = i * W + wave;
     if (piece < PIECES) ld128_lds(r, dst + piece * 1024, src(piece, lane));
   }
+  compiler_fence();
+}
+
+// What the output stage reads for the wave's rows, fetched early: lane
+// 48 + j fetches for row row0 + j (j < nrows).  Loads complete in issue
+// order, so the stream's vmcnt waits stay valid wherever this load sits: it
+// is either older than the load being waited for, or one more load after it
+// (the wait is then only stricter).
+template <typename Out>
+__device__ __forceinline__ typename Out::Pre prefetch_rows(const Out& out, int row0, int nrows, int lane) {
+  compiler_fence();
+  const auto p = out.prefetch(row0, lane & 15, lane >= 48 && (lane & 15) < nrows);
+  compiler_fence();
+  return p;
 }
 
 // Sum R per-lane row partials across the wave and hand row j (< nrows),
 // times `scale`, to the output stage as row row0 + j from lane 48 + j.
 template <int R, typename Out>
-__device__ __forceinline__ void store_rows(float (&acc)[R], const Out& out, int row0, int nrows, float scale,
-                                           int lane) {
+__device__ __forceinline__ void store_rows(float (&acc)[R], const Out& out, typename Out::Pre pre, int row0,
+                                           int nrows, float scale, int lane) {
   static_assert(R >= 1 && R <= 16, "one row per lane of the last 16-lane row");
   wave_reduce_dpp<R>(acc);
   const int j = lane & 15;
   float t = acc[0];
 #pragma unroll
   for (int s = 1; s < R; ++s) t = j == s ? acc[s] : t;
-  if (lane >= 48 && j < nrows) out.put(row0 + j, t * scale);
+  if (lane >= 48 && j < nrows) out.put(row0 + j, t * scale, pre);
 }
 
 // Shape -> (R rows per wave, W waves per workgroup) of a row-streaming

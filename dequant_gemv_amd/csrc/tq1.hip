@@ -263,6 +263,9 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   }
   wait_vm<S::kUpFront>();        // activations (issued first) are in LDS
   __builtin_amdgcn_s_barrier();  // ... every wave's pieces too
+  // the output stage's input for the wave's rows, after the barrier's wait
+  // (the stream's later waits only get stricter by this one load)
+  const auto pre = prefetch_rows(out, row0, nrows, lane);
   stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
 
   // Activation pairs of the lane's byte pairs: digit k of payload byte pos
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
     const float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0[sg]), acc[r]);
     acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1[sg]), t);
   });
-  store_rows<R>(acc, out, row0, nrows, 1.f, lane);
+  store_rows<R>(acc, out, pre, row0, nrows, 1.f, lane);
 }
 
 // Row materialisation.  Task t of an output row makes weights
