@@ -54,6 +54,7 @@ def _load():
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_get_rows.argtypes = [ctypes.c_int, P, I64, I64, P, I64, ctypes.c_int, P]
     lib.oracle_decode16.argtypes = [ctypes.c_int, P, I64, P]
+    lib.oracle_gemm.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, I64, P, I64, P, P]
     lib.oracle_tq1_digit.restype = ctypes.c_int
     lib.oracle_tq1_digit.argtypes = [ctypes.c_uint8, ctypes.c_int]
     lib.oracle_threads.restype = ctypes.c_int
@@ -154,6 +155,26 @@ def gemv(fmt: str, w: np.ndarray, x: np.ndarray, n: int, k: int, rows=None):
     a = np.empty(cnt, dtype=np.float64)
     if cnt:
         _load().oracle_gemv(FMT[fmt], _ptr(w), _ptr(x), n, k, rp, cnt, _ptr(y), _ptr(a))
+    return y, a
+
+
+def gemm(fmt: str, w: np.ndarray, x: np.ndarray, t: int, n: int, k: int, tokens=None, rows=None):
+    """Prefill form (Y = X . dequant(W)^T for T activation rows): (Y, A) of
+    shape [len(tokens), len(rows)] in fp64, A the sum of |x_i w_i| per output.
+    ``x`` holds [t][k] 16-bit codes; all tokens / rows when None."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(t, k)
+    tokens = np.arange(t) if tokens is None else np.asarray(tokens)
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    assert tokens.size == 0 or (tokens.min() >= 0 and tokens.max() < t)
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < n)
+    y = np.empty((tokens.size, rows.size), dtype=np.float64)
+    a = np.empty_like(y)
+    if y.size:
+        _load().oracle_gemm(FMT[fmt], _ptr(w), _ptr(x), t, n, k, _ptr(tokens), tokens.size, _ptr(rows),
+                            rows.size, _ptr(y), _ptr(a))
     return y, a
 
 

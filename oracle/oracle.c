@@ -25,6 +25,8 @@
  *         digit feeds) and "Not applicable" (digits from floor(3^k b / 256)).
  *  [DENSE] The Mojo "fp4_gemv" page compares against a dense bf16 GEMV of the
  *         same shape: w_i is the fp16 / bf16 value itself.
+ *  [PREFILL] Many activation rows at once (the Mojo page's M > 1 matmul path,
+ *         the TQ1_0 page's prefill): Y[t][r] = sum_i X[t][i] w[r][i].
  *  [ROWS] Materialising rows (the TQ1_0 page's dequantize template, the Mojo
  *         page's fp32 dequant): out = the fp32 weight, optionally cast to
  *         fp16 / bf16 with round-to-nearest-even.
@@ -310,5 +312,33 @@ void oracle_gemv(int fmt, const uint8_t* w, const uint16_t* x, int64_t n, int64_
     free(wr);
     y[t] = acc;
     a[t] = aacc;
+  }
+}
+
+/* Y[a][b] = sum_i X[tok[a]][i] w[row[b]][i] and A[a][b] = sum_i |X[tok[a]][i] w[row[b]][i]|
+ * for the listed activation rows (tokens) and weight rows: the prefill form,
+ * one plain GEMV per token.  X is [T][k] 16-bit codes (fp16, or bf16 for NVFP4
+ * and dense bf16). */
+void oracle_gemm(int fmt, const uint8_t* w, const uint16_t* x, int64_t t_count, int64_t n, int64_t k,
+                 const int64_t* tok, int64_t ntok, const int64_t* rows, int64_t nrows, double* y,
+                 double* a) {
+  const int x_bf16 = fmt == 1 || fmt == 4;
+  (void)t_count;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t b = 0; b < nrows; ++b) {
+    double* wr = (double*)malloc((size_t)k * sizeof(double));
+    dequant_row(fmt, w, n, k, rows[b], wr);
+    for (int64_t q = 0; q < ntok; ++q) {
+      const uint16_t* xt = x + tok[q] * k;
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t i = 0; i < k; ++i) {
+        double p = (x_bf16 ? oracle_bf16(xt[i]) : oracle_f16(xt[i])) * wr[i];
+        acc += p;
+        aacc += fabs(p);
+      }
+      y[q * nrows + b] = acc;
+      a[q * nrows + b] = aacc;
+    }
+    free(wr);
   }
 }
