@@ -131,6 +131,22 @@ int get_rows(Fmt f, const void* w, int64_t m, int64_t k, const int32_t* rows, in
   }
 }
 
+int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, int64_t k, hipStream_t s) {
+  int rc = check_shape(f, m, k);
+  if (rc != QGEMV_OK) return rc;
+  // the grid's y dimension counts tiles of 128 activation rows (at most 65535)
+  if (t < 0 || t > 65535 * int64_t(128) || k > qgemv::kPrefillMaxK) return QGEMV_E_SHAPE;
+  if (t == 0 || m == 0) return QGEMV_OK;
+  if (!w || !x || !y) return QGEMV_E_NULL;
+  if (misaligned(w, 16) || misaligned(x, 16) || misaligned(y, 4)) return QGEMV_E_ALIGN;
+  const int64_t yb = t * m * 4;
+  if (overlap(y, yb, w, weight_bytes(f, m, k)) || overlap(y, yb, x, t * k * 2)) return QGEMV_E_ALIAS;
+  switch (f) {
+    case kQ4k: return finish(qgemv::launch_q4k_prefill(w, x, y, t, m, k, s));
+    default: return QGEMV_E_SHAPE;
+  }
+}
+
 int dequant(Fmt f, const void* w, float* out, int64_t m, int64_t k, hipStream_t s) {
   int rc = check_shape(f, m, k);
   if (rc != QGEMV_OK) return rc;
@@ -199,6 +215,10 @@ int qget_rows_nvfp4(const void* w, int64_t M, int64_t K, const int32_t* rows, in
 int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
                   int32_t out_dtype, struct ihipStream_t* s) {
   return get_rows(kTq1, w, M, K, rows, nrows, out, out_dtype, s);
+}
+
+int qgemm_q4k(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
+  return gemm(kQ4k, w, x, y, T, M, K, s);
 }
 
 int64_t qgemv_read_sink_len(int64_t bytes) { return bytes > 0 ? qgemv::read_sink_len(bytes) : 0; }

@@ -166,6 +166,16 @@ __device__ __forceinline__ void wait_vm() {
   compiler_fence();
 }
 
+// Workgroup barrier that waits only for this wave's LDS accesses (lgkmcnt),
+// not for its outstanding global loads: __syncthreads() also waits vmcnt(0),
+// which would drain loads issued for later pipeline stages.
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One wave-wide 16-byte-per-lane buffer load straight into LDS: lane i's

@@ -33,7 +33,8 @@ GEMV_SYMBOLS = ("qgemv_q4k", "qgemv_nvfp4", "qgemv_tq1", "qgemv_f16", "qgemv_bf1
 GEMV_EX_SYMBOLS = ("qgemv_q4k_ex", "qgemv_nvfp4_ex", "qgemv_tq1_ex", "qgemv_f16_ex", "qgemv_bf16_ex")
 DEQUANT_SYMBOLS = ("qdequant_q4k", "qdequant_nvfp4", "qdequant_tq1")
 ROWS_SYMBOLS = ("qget_rows_q4k", "qget_rows_nvfp4", "qget_rows_tq1")
-ALL_SYMBOLS = GEMV_SYMBOLS + GEMV_EX_SYMBOLS + DEQUANT_SYMBOLS + ROWS_SYMBOLS + (
+GEMM_SYMBOLS = ("qgemm_q4k",)
+ALL_SYMBOLS = GEMV_SYMBOLS + GEMV_EX_SYMBOLS + DEQUANT_SYMBOLS + ROWS_SYMBOLS + GEMM_SYMBOLS + (
     "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror", "qgemv_last_hip_error",
     "qgemv_build_id")
 
@@ -74,6 +75,10 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [P, I64, I64, P, I64, P, ctypes.c_int32, P]
+    for name in GEMM_SYMBOLS:
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, P, I64, I64, I64, P]
     lib.qgemv_read_ceiling.restype = ctypes.c_int
     lib.qgemv_read_ceiling.argtypes = [P, I64, P, P]
     lib.qgemv_read_sink_len.restype = ctypes.c_int64
@@ -214,6 +219,12 @@ def qget_rows_tq1(w, M, K, rows, nrows, out, stream=None):
     return _get_rows("qget_rows_tq1", w, M, K, rows, nrows, out, stream)
 
 
+def qgemm_q4k(w, x, y, T, M, K, stream=None):
+    """Prefill: y[T][M] (fp32) = x[T][K] (fp16) . dequant_Q4_K(w)^T."""
+    _check(_lib.qgemm_q4k(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K), _stream(stream)), "qgemm_q4k")
+    return y
+
+
 def _dequant(name, w, out, M, K, stream):
     _check(getattr(_lib, name)(_addr(w), _addr(out), int(M), int(K), _stream(stream)), name)
     return out
@@ -255,6 +266,7 @@ GEMV_EX = {"q4k": qgemv_q4k_ex, "nvfp4": qgemv_nvfp4_ex, "tq1": qgemv_tq1_ex, "f
            "bf16": qgemv_bf16_ex}
 DEQUANT = {"q4k": qdequant_q4k, "nvfp4": qdequant_nvfp4, "tq1": qdequant_tq1}
 GET_ROWS = {"q4k": qget_rows_q4k, "nvfp4": qget_rows_nvfp4, "tq1": qget_rows_tq1}
+GEMM = {"q4k": qgemm_q4k}
 
 
 def gemv(fmt: str, w, x, M: int, K: int, y=None, stream=None):
@@ -296,3 +308,11 @@ def get_rows(fmt: str, w, M: int, K: int, rows=None, nrows=None, dtype="f16", ou
     if out is None:
         out = torch.empty((nrows, K), dtype=_torch_dtype(dtype), device=w.device)
     return GET_ROWS[fmt](w, M, K, rows, nrows, out, stream)
+
+
+def gemm(fmt: str, w, x, T: int, M: int, K: int, y=None, stream=None):
+    import torch
+
+    if y is None:
+        y = torch.empty((T, M), dtype=torch.float32, device=w.device)
+    return GEMM[fmt](w, x, y, T, M, K, stream)

@@ -141,6 +141,18 @@ int qget_rows_nvfp4(const void* w, int64_t M, int64_t K, const int32_t* rows, in
 int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int64_t nrows, void* out,
                   int32_t out_dtype, struct ihipStream_t* stream);
 
+/* Prefill: T activation rows at once (the Mojo fp4_gemv page's M > 1 matmul
+ * path; the TQ1_0 page's prefill):
+ *     y[t][r] = sum_{i<K} x[t][i] * dequant(W)[r][i]     t < T, r < M
+ * x is [T][K] row-major in the format's activation type (fp16 for Q4_K), y is
+ * [T][M] row-major fp32.  W, M and K as for the GEMV of the same format, plus
+ * K <= 2^22 and T <= 65535 * 128.  The weights are dequantised to the
+ * activation type (one rounding per weight) and multiplied on the matrix
+ * cores with fp32 accumulation.  T == 0 or M == 0 is a successful no-op; y
+ * must not overlap W or x. */
+int qgemm_q4k(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
+              struct ihipStream_t* stream);
+
 /* fp32 materialisation out[M][K] of the same formats (same W conventions as
  * above; the same as qget_rows_* with rows = NULL, nrows = M, QGEMV_F32).  Each value is the correctly rounded fp32 of the exact weight, which
  * for these formats is the exact weight itself whenever it is representable

@@ -1,0 +1,70 @@
+"""Parity of the prefill entry points (many activation rows, matrix cores)
+with the fp64 oracle's Y = X . dequant(W)^T.
+
+Bar: |y - y_ref| <= 1e-3 * sum_i |x_i w_i| + 1e-5 per output.  The weights
+enter the matrix unit rounded once to the activation type (relative error at
+most 2^-11 for fp16, 2^-8 for bf16, the latter only for NVFP4 whose weights
+are exact in bf16), which stays inside that bound; accumulation is fp32.
+Shapes cover single tokens, ragged token and row tiles, several K steps and
+the Llama-8B prefill shapes (sampled outputs there).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dequant_gemv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def q():
+    from dequant_gemv_amd import qgemv
+
+    return qgemv
+
+
+def _x(fmt, t, k, seed):
+    return np.stack([synth.activations(fmt, k, seed + i) for i in range(t)])
+
+
+CASES = [
+    # (format, T, M, K, sampled tokens, sampled rows)
+    ("q4k", 1, 64, 256, None, None),
+    ("q4k", 5, 300, 2304, None, None),
+    ("q4k", 128, 128, 512, None, None),
+    ("q4k", 200, 520, 4096, None, None),
+    ("q4k", 130, 4096, 4096, 40, 300),
+    ("q4k", 512, 4096, 14336, 24, 200),
+    ("q4k", 512, 14336, 4096, 24, 300),
+]
+
+
+@pytest.mark.parametrize("fmt,t,m,k,st,sr", CASES)
+def test_prefill(q, fmt, t, m, k, st, sr):
+    seed = 700 + t + m % 97 + k % 89
+    w = synth.weights(fmt, m, k, synth.W_SEED + seed)
+    x = _x(fmt, t, k, synth.X_SEED + seed)
+    y = torch.full((t, m), float("nan"), dtype=torch.float32, device=DEV)
+    q.GEMM[fmt](torch.from_numpy(w).to(DEV), torch.from_numpy(x.view(np.int16).copy()).to(DEV), y, t, m, k)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    toks = np.arange(t) if st is None else np.unique(np.concatenate([[0, t - 1], rng.integers(0, t, st)]))
+    rows = np.arange(m) if sr is None else np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, sr)]))
+    yr, ar = oracle.gemm(fmt, w, x, t, m, k, tokens=toks, rows=rows)
+    g = got[np.ix_(toks, rows)]
+    bad = np.argwhere(~(np.abs(g - yr) <= 1e-3 * ar + 1e-5))
+    assert bad.size == 0, (f"{fmt} T={t} {m}x{k}: {len(bad)} outputs off, e.g. token {toks[bad[0][0]]} row "
+                           f"{rows[bad[0][1]]}: {g[tuple(bad[0])]} vs {yr[tuple(bad[0])]}")
+
+
+def test_prefill_empty_is_noop(q):
+    w = torch.zeros(144, dtype=torch.uint8, device=DEV)
+    y = torch.zeros(1, device=DEV)
+    q.qgemm_q4k(w, w, y, 0, 1, 256)
+    q.qgemm_q4k(w, w, y, 3, 0, 256)
+    torch.cuda.synchronize()
