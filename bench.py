@@ -12,8 +12,8 @@ Printed: ONE JSON line with the metric (achieved HBM GB/s of the kernel over
 the algorithmic bytes weights + x + y), the roofline object of the dominant
 kernel, the CPU baseline (the fp64 oracle on the host cores) and extra context
 (pure-read ceiling over the same bytes, the other formats' shapes, the dense
-bf16 GEMV of the same shape, the general output stage, row materialisation and
-a Llama-8B per-token sweep).
+bf16 GEMV of the same shape, the general output stage, row materialisation,
+prefill on the matrix cores and a Llama-8B per-token sweep).
 """
 from __future__ import annotations
 
@@ -377,6 +377,72 @@ def measure_rows(steps, warmup, rotate):
     return out
 
 
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of the part
+
+PREFILL_CASES = [
+    # (format, tokens, weight rows, K)
+    ("q4k", 512, 4096, 14336), ("q4k", 512, 14336, 4096), ("q4k", 4096, 14336, 4096),
+    ("nvfp4", 512, 4096, 14336), ("nvfp4", 512, 14336, 4096),
+    ("tq1", 512, 4096, 14336), ("tq1", 512, 14336, 4096),
+]
+
+
+def measure_prefill(steps, warmup):
+    """Prefill (many tokens): y = X . dequant(W)^T on the matrix cores, in
+    TFLOP/s of 2 T N K flops; for Q4_K also the unfused path (materialise W
+    as fp16 with the row kernel, then the library fp16 GEMM) for comparison."""
+    import numpy as np
+    import torch
+
+    from dequant_gemv_amd import qgemv, synth
+
+    dev = torch.device("cuda:0")
+    out = {}
+    stream = torch.cuda.Stream()
+    for fmt, t, n, k in PREFILL_CASES:
+        w0 = torch.from_numpy(synth.weights(fmt, n, k, 4200)).to(dev)
+        ws = [w0] + [w0.clone() for _ in range(3)]
+        xs = np.stack([synth.activations(fmt, k, 4300 + i) for i in range(t)])
+        x = torch.from_numpy(xs.view(np.int16)).to(dev)
+        y = torch.empty((t, n), dtype=torch.float32, device=dev)
+        fn = qgemv.GEMM[fmt]
+        us = time_graph(lambda i, h: fn(ws[i], x, y, t, n, k, h), 4, max(16, steps // 80), max(8, warmup // 80), stream)
+        flops = 2.0 * t * n * k
+        rec = {
+            "workload": f"{fmt} prefill, {t} tokens x {n} rows x K {k}",
+            "us": round(us, 2),
+            "tflops": round(flops / us / 1e6, 1),
+            "pct_of_mfma_peak": round(100 * flops / us / 1e6 / MFMA_PEAK_TFLOPS, 1),
+        }
+        if fmt == "q4k":
+            wf = torch.empty((n, k), dtype=torch.float16, device=dev)
+            us_rows = time_graph(lambda i, h: qgemv.qget_rows_q4k(ws[i], n, k, None, n, wf, h), 4,
+                                 max(16, steps // 80), max(8, warmup // 80), stream)
+            xf = x.view(torch.float16)
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    torch.matmul(xf, wf.t())
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            with torch.cuda.stream(stream):
+                for _ in range(10):
+                    torch.matmul(xf, wf.t())
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            us_mm = 1e3 * ev0.elapsed_time(ev1) / 10
+            rec["unfused_us"] = round(us_rows + us_mm, 2)
+            rec["unfused_note"] = (f"fp16 materialisation {us_rows:.1f} us + library fp16 GEMM {us_mm:.1f} us "
+                                   f"({flops / us_mm / 1e6:.0f} TFLOP/s)")
+            del wf
+        out[f"{fmt}_{t}x{n}x{k}"] = rec
+        log(f"[bench] prefill {fmt} T={t} {n}x{k}: {us:.1f} us, {rec['tflops']} TFLOP/s"
+            + (f" (unfused {rec['unfused_us']} us)" if "unfused_us" in rec else ""))
+        del ws, x, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(fmt, n, k, budget_s=10.0):
     """The fp64 oracle as it stands, all host cores, on the same workload."""
     import numpy as np
@@ -484,11 +550,12 @@ def main():
         }
         log(f"[bench] NVFP4 vs bf16 at 4096x14336: {fp4_vs_bf16['speedup']}x")
 
-    epilogue = rows_res = None
+    epilogue = rows_res = prefill_res = None
     if not args.no_extra and not args.fmt:
         epilogue = measure_epilogue(max(args.rotate, args.steps // 4), args.warmup, args.rotate)
         log(f"[bench] epilogue: {epilogue['us_per_gemv']} us (plain {epilogue['us_per_gemv_plain_fp32']} us)")
         rows_res = measure_rows(args.steps, args.warmup, args.rotate)
+        prefill_res = measure_prefill(args.steps, args.warmup)
 
     sweeps = {}
     if not args.no_extra and not args.fmt and args.sweep != "none":
@@ -541,6 +608,7 @@ def main():
         "fp4_vs_bf16": fp4_vs_bf16,
         "epilogue": epilogue,
         "get_rows": rows_res,
+        "prefill": prefill_res,
         "decode_sweep": sweeps,
         "build_id": have,
         "gpu": torch.cuda.get_device_name(0),

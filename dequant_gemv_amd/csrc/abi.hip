@@ -136,6 +136,7 @@ int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, in
   if (rc != QGEMV_OK) return rc;
   // the grid's y dimension counts tiles of 128 activation rows (at most 65535)
   if (t < 0 || t > 65535 * int64_t(128) || k > qgemv::kPrefillMaxK) return QGEMV_E_SHAPE;
+  if (f == kNvfp4 && k % 64 != 0) return QGEMV_E_SHAPE;  // whole 64-weight steps
   if (t == 0 || m == 0) return QGEMV_OK;
   if (!w || !x || !y) return QGEMV_E_NULL;
   if (misaligned(w, 16) || misaligned(x, 16) || misaligned(y, 4)) return QGEMV_E_ALIGN;
@@ -143,6 +144,8 @@ int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, in
   if (overlap(y, yb, w, weight_bytes(f, m, k)) || overlap(y, yb, x, t * k * 2)) return QGEMV_E_ALIAS;
   switch (f) {
     case kQ4k: return finish(qgemv::launch_q4k_prefill(w, x, y, t, m, k, s));
+    case kNvfp4: return finish(qgemv::launch_nvfp4_prefill(w, x, y, t, m, k, s));
+    case kTq1: return finish(qgemv::launch_tq1_prefill(w, x, y, t, m, k, s));
     default: return QGEMV_E_SHAPE;
   }
 }
@@ -219,6 +222,12 @@ int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int6
 
 int qgemm_q4k(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
   return gemm(kQ4k, w, x, y, T, M, K, s);
+}
+int qgemm_nvfp4(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
+  return gemm(kNvfp4, w, x, y, T, M, K, s);
+}
+int qgemm_tq1(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
+  return gemm(kTq1, w, x, y, T, M, K, s);
 }
 
 int64_t qgemv_read_sink_len(int64_t bytes) { return bytes > 0 ? qgemv::read_sink_len(bytes) : 0; }

@@ -176,6 +176,20 @@ __device__ __forceinline__ void lds_barrier() {
   compiler_fence();
 }
 
+// Base-3 digit of two bytes at once (the 16-bit halves of q): digit k of a
+// TQ1_0 byte b is ((3^k b) mod 256) * 3 >> 8 ("metal: TQ1_0 kernel
+// performance", section "Not applicable"); p = 3^k.
+__device__ __forceinline__ u16x2 tq1_digits2(u16x2 q, unsigned short p) {
+  const u16x2 m = (q * u16x2{p, p}) & u16x2{0xFF, 0xFF};
+  return (m * u16x2{3, 3}) >> u16x2{8, 8};
+}
+
+// 3^k for k = 0..4 without branches: 1, 3, 9, 27 are the bytes of one word.
+__device__ __forceinline__ unsigned short pow3_u16(int k) {
+  const unsigned lo = (0x1B090301u >> (8 * (k & 3))) & 0xFFu;
+  return (unsigned short)(k >= 4 ? 81u : lo);
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One wave-wide 16-byte-per-lane buffer load straight into LDS: lane i's

@@ -34,6 +34,9 @@ hipError_t launch_tq1_get_rows(const void* w, int64_t n, int64_t k, const int32_
 // Prefill: y[t][r] (fp32, [T][n]) = x[t] . dequant(W)[r] for T activation rows.
 constexpr int64_t kPrefillMaxK = int64_t(1) << 22;
 hipError_t launch_q4k_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_nvfp4_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
+                                hipStream_t s);
+hipError_t launch_tq1_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s);
 hipError_t launch_read_ceiling(const void* buf, int64_t bytes, float* sink, hipStream_t s);
 int64_t read_sink_len(int64_t bytes);
 

@@ -60,17 +60,26 @@ __device__ __forceinline__ unsigned pf_pack2(float a, float b) {
 struct Q4kPrefill {
   using T = _Float16;
   static constexpr bool kBf16 = false;
+  static constexpr int kKMultiple = 256;
+  static constexpr bool kWaveHalf = false;  // neighbouring lanes: the two halves of one row
+  struct Desc {
+    __amdgpu_buffer_rsrc_t r;  // the tile's rows
+    uint32_t row_bytes;
+  };
   struct Raw {
     u32x4 hdr, q0, q1;
   };
-  static __host__ __device__ int64_t row_bytes(int64_t k) { return k / 256 * 144; }
-  static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int s, int) {
-    const uint32_t blk = row_off + (uint32_t)(s >> 2) * 144u;
+  static __device__ __forceinline__ Desc desc(const uint8_t* w, int, int k, int n0, int nv) {
+    const uint32_t rb = (uint32_t)(k / 256 * 144);
+    return Desc{make_rsrc(w + (int64_t)n0 * rb, (uint32_t)nv * rb), rb};
+  }
+  static __device__ __forceinline__ Raw load(const Desc& d, int r, int s, int) {
+    const uint32_t blk = (uint32_t)r * d.row_bytes + (uint32_t)(s >> 2) * 144u;
     const uint32_t qo = blk + 16u + 32u * (uint32_t)(s & 3);
     Raw raw;
-    raw.hdr = ld128(r, blk);
-    raw.q0 = ld128(r, qo);
-    raw.q1 = ld128(r, qo + 16u);
+    raw.hdr = ld128(d.r, blk);
+    raw.q0 = ld128(d.r, qo);
+    raw.q1 = ld128(d.r, qo + 16u);
     return raw;
   }
   static __device__ __forceinline__ void make(const Raw& raw, int s, int h, unsigned (&out)[16]) {
@@ -94,6 +103,123 @@ struct Q4kPrefill {
       const float w3 = __builtin_fmaf(ds, (float)(v >> 24), -dm);
       out[2 * i] = pf_pack2<T>(w0, w1);
       out[2 * i + 1] = pf_pack2<T>(w2, w3);
+    }
+  }
+};
+
+// NVFP4 (Mojo module "fp4_gemv"): step s, half h = weights [64 s + 32 h, +32)
+// of a row: 16 nibble bytes and the 2 scale bytes of their two 16-weight
+// blocks.  Every e2m1 * |scale| is exact in fp32 and in bf16, so the bf16
+// weights are exact and the MFMA runs on bf16 (the activations' type).
+struct Nvfp4Prefill {
+  using T = __bf16;
+  static constexpr bool kBf16 = true;
+  static constexpr int kKMultiple = 64;
+  static constexpr bool kWaveHalf = false;
+  struct Desc {
+    __amdgpu_buffer_rsrc_t nib, sc;  // the tile's nibble rows, its scale rows
+    uint32_t nib_row, sc_row;
+  };
+  struct Raw {
+    u32x4 q;
+    unsigned short sc;
+  };
+  static __device__ __forceinline__ Desc desc(const uint8_t* w, int n, int k, int n0, int nv) {
+    const uint32_t nr = (uint32_t)(k / 2), sr = (uint32_t)(k / 16);
+    return Desc{make_rsrc(w + (int64_t)n0 * nr, (uint32_t)nv * nr),
+                make_rsrc(w + (int64_t)n * nr + (int64_t)n0 * sr, (uint32_t)nv * sr), nr, sr};
+  }
+  static __device__ __forceinline__ Raw load(const Desc& d, int r, int s, int h) {
+    Raw raw;
+    raw.q = ld128(d.nib, (uint32_t)r * d.nib_row + 32u * (uint32_t)s + 16u * (uint32_t)h);
+    raw.sc = ld16(d.sc, (uint32_t)r * d.sc_row + 4u * (uint32_t)s + 2u * (uint32_t)h);
+    return raw;
+  }
+  static __device__ __forceinline__ void make(const Raw& raw, int, int, unsigned (&out)[16]) {
+    const float s0 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)raw.sc, 0));
+    const float s1 = __builtin_fabsf(__builtin_amdgcn_cvt_f32_fp8((int)raw.sc, 1));
+    const unsigned q[4] = {raw.q.x, raw.q.y, raw.q.z, raw.q.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // byte i: weights 2i, 2i + 1 (block i / 8)
+      const f32x2 e = fp4x2_f32(q[i >> 2], i);
+      const float sc = i < 8 ? s0 : s1;
+      out[i] = pf_pack2<T>(e.x * sc, e.y * sc);
+    }
+  }
+};
+
+
+// TQ1_0 ("metal: TQ1_0 kernel performance", sections 1, 2 and "Not
+// applicable"): step s covers elements [64 c, 64 c + 64) of block b = s / 4
+// (c = s % 4); half h the 32 starting at e0 = 64 c + 32 h, which are one
+// digit of qs[0..31] (e0 < 160), two digits of qs[32..47] (e0 = 160, 192),
+// or digit 4 of qs[32..47] followed by the four digits of qh[0..3] (e0 =
+// 224).  The block is only 2-byte aligned, so the bytes from qs[0] (or
+// qs[32]) on are read as nine aligned dwords (single-dword loads: one past
+// the range reads zero and is never needed) and realigned with alignbyte; d
+// is a 16-bit load.  Each weight is one of d * -1, d * 0, d * 1, exact in
+// fp16: two weights' digits come from one packed 16-bit multiply and one
+// byte permute picks their fp16 codes (as in the row materialisation).
+struct Tq1Prefill {
+  using T = _Float16;
+  static constexpr bool kBf16 = false;
+  static constexpr int kKMultiple = 256;
+  static constexpr bool kWaveHalf = true;  // make() branches on the half: one half per wave
+  struct Desc {
+    __amdgpu_buffer_rsrc_t r;  // the tile's rows
+    uint32_t row_bytes;
+  };
+  struct Raw {
+    unsigned wd[9];
+    unsigned short d;
+    unsigned char sh;  // bytes to drop at the front of the window
+  };
+  static __device__ __forceinline__ Desc desc(const uint8_t* w, int, int k, int n0, int nv) {
+    const uint32_t rb = (uint32_t)(k / 256 * 54);
+    return Desc{make_rsrc(w + (int64_t)n0 * rb, (uint32_t)nv * rb), rb};
+  }
+  static __device__ __forceinline__ Raw load(const Desc& d, int r, int s, int h) {
+    const uint32_t blk = (uint32_t)r * d.row_bytes + (uint32_t)(s >> 2) * 54u;
+    const int e0 = 64 * (s & 3) + 32 * h;
+    const uint32_t a = blk + (e0 < 160 ? 0u : 32u);
+    const uint32_t al = a & ~3u;
+    Raw raw;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) raw.wd[i] = ld32(d.r, al + 4u * (uint32_t)i);
+    raw.d = ld16(d.r, blk + 52u);
+    raw.sh = (unsigned char)(a & 3u);
+    return raw;
+  }
+  // weights (2 pr, 2 pr + 1) from bytes bi, bi + 1 of the stream, digit k
+  static __device__ __forceinline__ unsigned pair(const unsigned (&q)[8], int bi, int k, unsigned vm, unsigned vp) {
+    const unsigned word = q[bi >> 2];
+    const unsigned b = (unsigned)(bi & 3);
+    const unsigned pr = __builtin_amdgcn_perm(0u, word, 0x0C000C00u | b | ((b + 1u) << 16));
+    const u16x2 dg = tq1_digits2(__builtin_bit_cast(u16x2, pr), pow3_u16(k));
+    const u16x2 sel = dg * u16x2{0x0202, 0x0202} + u16x2{0x0100, 0x0100};
+    return __builtin_amdgcn_perm(vp, vm, __builtin_bit_cast(unsigned, sel));
+  }
+  static __device__ __forceinline__ void make(const Raw& raw, int s, int h, unsigned (&out)[16]) {
+    unsigned q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_alignbyte(raw.wd[j + 1], raw.wd[j], raw.sh);
+    const float d = (float)__builtin_bit_cast(_Float16, raw.d);
+    const unsigned vm = pf_pack2<T>(d * -1.f, d * 0.f);  // codes of d*(t-1), t = 0, 1
+    const unsigned vp = pf_pack2<T>(d * 1.f, 0.f);        // and t = 2
+    const int e0 = 64 * (s & 3) + 32 * h;  // the same for the whole wave
+    if (e0 < 160) {
+      const int k = e0 >> 5;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) out[p] = pair(q, 2 * p, k, vm, vp);
+    } else if (e0 < 224) {
+      const int k0 = (e0 - 160) >> 4;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) out[p] = pair(q, (2 * p) & 15, k0 + (p >> 3), vm, vp);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) out[p] = pair(q, 2 * p, 4, vm, vp);
+#pragma unroll
+      for (int p = 8; p < 16; ++p) out[p] = pair(q, 16 + ((2 * p - 16) & 3), (2 * p - 16) >> 2, vm, vp);
     }
   }
 };
@@ -132,15 +258,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint8_t* __restri
   // activations of the tile: rows t0.. (zero past T); weights: rows n0.. (zero past n)
   const int tv = min(kPfBT, t_count - t0), nv = min(kPfBN, n - n0);
   const auto xr = make_rsrc(x + (int64_t)t0 * k, (uint32_t)tv * xrow);
-  const int64_t rb = F::row_bytes(k);
-  const auto wr = make_rsrc(w + (int64_t)n0 * rb, (uint32_t)(nv * rb));
+  const typename F::Desc wd = F::desc(w, n, k, n0, nv);
 
-  // this thread's slots: tile row r = tid / 2, half h: activation granules
-  // 4h .. 4h + 3 of row r (64 contiguous bytes) and weights [32 h, 32 h + 32)
-  // of weight row r
-  const int dr = tid >> 1, dh = tid & 1;
-  const uint32_t drow = (uint32_t)(dr * rb);
-  const uint32_t xoff = (uint32_t)dr * xrow + 64u * (uint32_t)dh;
+  // this thread's slots: activation granules 4 xh .. 4 xh + 3 of tile row
+  // xr_ = tid / 2 (64 contiguous bytes), and weights [32 dh, 32 dh + 32) of
+  // weight row dr: the two halves of a row on neighbouring lanes (their
+  // packed bytes are next to each other), or, for a format whose
+  // dequantisation branches on the half, one half per wave
+  const int xr_ = tid >> 1, xh = tid & 1;
+  const int dr = F::kWaveHalf ? (tid & 127) : (tid >> 1), dh = F::kWaveHalf ? (tid >> 7) : (tid & 1);
+  const uint32_t xoff = (uint32_t)xr_ * xrow + 64u * (uint32_t)xh;
 
   struct XRaw {
     u32x4 g[4];
@@ -154,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint8_t* __restri
   auto store_x = [&](const XRaw& v, int b) {
     unsigned char* const base = xs0 + b * kPfTile;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + pf_off(dr, 4 * dh + i)) = v.g[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + pf_off(xr_, 4 * xh + i)) = v.g[i];
   };
   auto store_w = [&](const unsigned (&v)[16], int b) {
     unsigned char* const base = ws0 + b * kPfTile;
@@ -180,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint8_t* __restri
   for (int p = 0; p < P; ++p)
     if (p < steps) {
       xq[p] = load_x(p);
-      wq[p] = F::load(wr, drow, s_begin + p, dh);
+      wq[p] = F::load(wd, dr, s_begin + p, dh);
     }
   {
     store_x(xq[0], 0);
@@ -200,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint8_t* __restri
         // end these are harmless range-checked reads and the last step's
         // stores go to a stage nobody reads.
         xq[I] = load_x(s + P);
-        wq[I] = F::load(wr, drow, s_begin + s + P, dh);
+        wq[I] = F::load(wd, dr, s_begin + s + P, dh);
         const unsigned char* const xb = xs0 + (s & 1) * kPfTile;
         const unsigned char* const wb = ws0 + (s & 1) * kPfTile;
         // step s + 1's dequantisation, interleaved below with this step's MFMAs
@@ -303,6 +430,13 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
 
 hipError_t launch_q4k_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s) {
   return launch_prefill<Q4kPrefill>(w, x, y, t, n, k, s);
+}
+hipError_t launch_nvfp4_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
+                                hipStream_t s) {
+  return launch_prefill<Nvfp4Prefill>(w, x, y, t, n, k, s);
+}
+hipError_t launch_tq1_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s) {
+  return launch_prefill<Tq1Prefill>(w, x, y, t, n, k, s);
 }
 
 }  // namespace qgemv

@@ -350,10 +350,6 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
 // register, packed 16-bit multiplies give digit = ((3^k * q) mod 256) * 3 >> 8
 // ("Not applicable" section of the TQ1_0 page) for both, and one v_perm_b32
 // picks each half's 2 output bytes out of the 6-byte table (-d, 0d, +d).
-__device__ __forceinline__ u16x2 tq1_digits2(u16x2 q, unsigned short p) {
-  const u16x2 m = (q * u16x2{p, p}) & u16x2{0xFF, 0xFF};
-  return (m * u16x2{3, 3}) >> u16x2{8, 8};
-}
 
 #ifndef QGEMV_TQ1_ROWS_U
 #define QGEMV_TQ1_ROWS_U 2  // row-materialisation tasks per thread
@@ -374,11 +370,7 @@ __global__ __launch_bounds__(256) void tq1_rows_kernel(const uint8_t* __restrict
   // the row's bytes (the row is the same for the whole workgroup)
   const auto wr = make_rsrc(w + (int64_t)(r < 0 ? 0 : r) * nb * kTq1Bytes, r < 0 ? 0u : (uint32_t)(nb * kTq1Bytes));
   T* const orow = out + (int64_t)j * nb * 256;
-  // 3^k for k = 0..4 without branches: 1, 3, 9, 27 are the bytes of one word
-  auto pow3 = [](int k) -> unsigned short {
-    const unsigned lo = (0x1B090301u >> (8 * (k & 3))) & 0xFFu;
-    return (unsigned short)(k >= 4 ? 81u : lo);
-  };
+  auto pow3 = [](int k) { return pow3_u16(k); };
   rows_thread<U, Tq1RowIn>(
       bpr, nb * (256 / E), r >= 0,
       [&](int t) {

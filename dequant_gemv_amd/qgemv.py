@@ -33,7 +33,7 @@ GEMV_SYMBOLS = ("qgemv_q4k", "qgemv_nvfp4", "qgemv_tq1", "qgemv_f16", "qgemv_bf1
 GEMV_EX_SYMBOLS = ("qgemv_q4k_ex", "qgemv_nvfp4_ex", "qgemv_tq1_ex", "qgemv_f16_ex", "qgemv_bf16_ex")
 DEQUANT_SYMBOLS = ("qdequant_q4k", "qdequant_nvfp4", "qdequant_tq1")
 ROWS_SYMBOLS = ("qget_rows_q4k", "qget_rows_nvfp4", "qget_rows_tq1")
-GEMM_SYMBOLS = ("qgemm_q4k",)
+GEMM_SYMBOLS = ("qgemm_q4k", "qgemm_nvfp4", "qgemm_tq1")
 ALL_SYMBOLS = GEMV_SYMBOLS + GEMV_EX_SYMBOLS + DEQUANT_SYMBOLS + ROWS_SYMBOLS + GEMM_SYMBOLS + (
     "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror", "qgemv_last_hip_error",
     "qgemv_build_id")
@@ -225,6 +225,19 @@ def qgemm_q4k(w, x, y, T, M, K, stream=None):
     return y
 
 
+def qgemm_nvfp4(w, x, y, T, M, K, stream=None):
+    """Prefill: y[T][M] (fp32) = x[T][K] (bf16) . dequant_NVFP4(w)^T."""
+    _check(_lib.qgemm_nvfp4(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K), _stream(stream)),
+           "qgemm_nvfp4")
+    return y
+
+
+def qgemm_tq1(w, x, y, T, M, K, stream=None):
+    """Prefill: y[T][M] (fp32) = x[T][K] (fp16) . dequant_TQ1_0(w)^T."""
+    _check(_lib.qgemm_tq1(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K), _stream(stream)), "qgemm_tq1")
+    return y
+
+
 def _dequant(name, w, out, M, K, stream):
     _check(getattr(_lib, name)(_addr(w), _addr(out), int(M), int(K), _stream(stream)), name)
     return out
@@ -266,7 +279,7 @@ GEMV_EX = {"q4k": qgemv_q4k_ex, "nvfp4": qgemv_nvfp4_ex, "tq1": qgemv_tq1_ex, "f
            "bf16": qgemv_bf16_ex}
 DEQUANT = {"q4k": qdequant_q4k, "nvfp4": qdequant_nvfp4, "tq1": qdequant_tq1}
 GET_ROWS = {"q4k": qget_rows_q4k, "nvfp4": qget_rows_nvfp4, "tq1": qget_rows_tq1}
-GEMM = {"q4k": qgemm_q4k}
+GEMM = {"q4k": qgemm_q4k, "nvfp4": qgemm_nvfp4, "tq1": qgemm_tq1}
 
 
 def gemv(fmt: str, w, x, M: int, K: int, y=None, stream=None):

@@ -152,6 +152,15 @@ int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int6
  * must not overlap W or x. */
 int qgemm_q4k(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
               struct ihipStream_t* stream);
+/* NVFP4 prefill: x is [T][K] bf16; K % 64 == 0.  The weights e2m1 * |scale|
+ * are exact in bf16, so the matrix cores see them unrounded. */
+int qgemm_nvfp4(const void* w, const void* x_bf16, float* y, int64_t T, int64_t M, int64_t K,
+                struct ihipStream_t* stream);
+/* TQ1_0 prefill: x is [T][K] fp16.  The weights d * (t - 1) are exact in
+ * fp16 ("metal: TQ1_0 kernel performance", section "Prefill": the block is
+ * unpacked a whole 64-weight step at a time). */
+int qgemm_tq1(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
+              struct ihipStream_t* stream);
 
 /* fp32 materialisation out[M][K] of the same formats (same W conventions as
  * above; the same as qget_rows_* with rows = NULL, nrows = M, QGEMV_F32).  Each value is the correctly rounded fp32 of the exact weight, which

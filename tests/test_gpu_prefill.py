@@ -40,6 +40,17 @@ CASES = [
     ("q4k", 130, 4096, 4096, 40, 300),
     ("q4k", 512, 4096, 14336, 24, 200),
     ("q4k", 512, 14336, 4096, 24, 300),
+    ("nvfp4", 1, 64, 64, None, None),
+    ("nvfp4", 5, 300, 2112, None, None),
+    ("nvfp4", 200, 520, 4096, None, None),
+    ("nvfp4", 512, 4096, 14336, 24, 200),
+    ("nvfp4", 512, 14336, 4096, 24, 300),
+    ("tq1", 1, 64, 256, None, None),
+    ("tq1", 5, 300, 2304, None, None),
+    ("tq1", 200, 520, 4096, None, None),
+    ("tq1", 131, 77, 1280, None, None),
+    ("tq1", 512, 4096, 14336, 24, 200),
+    ("tq1", 512, 14336, 4096, 24, 300),
 ]
 
 
