@@ -48,6 +48,24 @@ __device__ __forceinline__ unsigned ld32(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ unsigned short ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
+// The same with a wave-uniform part of the offset in an SGPR (soff): the
+// range check covers voff + soff, which must not exceed 2^32.
+__device__ __forceinline__ u32x4 ld128s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)__builtin_amdgcn_readfirstlane(soff), 0);
+}
+__device__ __forceinline__ unsigned ld32s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)__builtin_amdgcn_readfirstlane(soff), 0);
+}
+__device__ __forceinline__ unsigned short ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)__builtin_amdgcn_readfirstlane(soff), 0);
+}
+__device__ __forceinline__ unsigned char ld8s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)__builtin_amdgcn_readfirstlane(soff), 0);
+}
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+__device__ __forceinline__ u32x2 ld64s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)__builtin_amdgcn_readfirstlane(soff), 0);
+}
 
 __device__ __forceinline__ f16x2 as_h2(unsigned v) { return __builtin_bit_cast(f16x2, v); }
 
@@ -199,6 +217,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 template <int AUX = 0>
 __device__ __forceinline__ void ld128_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, AUX);
+}
+// The same with a wave-uniform part of the offset in an SGPR (see ld128s).
+__device__ __forceinline__ void ld128_lds_s(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, (int)__builtin_amdgcn_readfirstlane(soff), 0,
+                                           0);
 }
 
 // Compile-time loop: calls f(Int<I>{}) for I = B .. E-1, so the body can use

@@ -72,6 +72,33 @@ def test_gemv_validation(q, name, kmul, kmax):
     assert f(W, X, X, 4, kmul, None) == q.QGEMV_E_ALIAS
 
 
+GEMMS = [("qgemm_q4k", 256), ("qgemm_nvfp4", 64), ("qgemm_tq1", 256)]
+
+
+@pytest.mark.parametrize("name,kmul", GEMMS)
+def test_gemm_validation(q, name, kmul):
+    f = getattr(q.lib(), name)
+    W, X, Y = A, A + (1 << 36), A + (2 << 36)
+    assert f(W, X, Y, -1, 4, kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 65535 * 128 + 1, 4, kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 3, -1, kmul, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 3, 4, 0, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 3, 4, kmul + kmul // 2, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 3, 4, (1 << 21) + 256, None) == q.QGEMV_E_SHAPE  # K limit of the prefill
+    if name == "qgemm_nvfp4":
+        assert f(W, X, Y, 3, 4, 96, None) == q.QGEMV_E_SHAPE  # whole 64-weight steps
+    assert f(W, X, Y, 0, 4, kmul, None) == q.QGEMV_OK  # empty: no-op, no launch
+    assert f(W, X, Y, 3, 0, kmul, None) == q.QGEMV_OK
+    assert f(None, X, Y, 3, 4, kmul, None) == q.QGEMV_E_NULL
+    assert f(W, None, Y, 3, 4, kmul, None) == q.QGEMV_E_NULL
+    assert f(W, X, None, 3, 4, kmul, None) == q.QGEMV_E_NULL
+    assert f(W + 8, X, Y, 3, 4, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, X + 2, Y, 3, 4, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, X, Y + 2, 3, 4, kmul, None) == q.QGEMV_E_ALIGN
+    assert f(W, X, W + 16, 3, 4, kmul, None) == q.QGEMV_E_ALIAS
+    assert f(W, X, X + 4, 3, 4, kmul, None) == q.QGEMV_E_ALIAS
+
+
 @pytest.mark.parametrize("name,kmul,kmax", GEMVS)
 def test_gemv_ex_validation(q, name, kmul, kmax):
     f = getattr(q.lib(), name + "_ex")

@@ -5,8 +5,9 @@ Bar: |y - y_ref| <= 1e-3 * sum_i |x_i w_i| + 1e-5 per output.  The weights
 enter the matrix unit rounded once to the activation type (relative error at
 most 2^-11 for fp16, 2^-8 for bf16, the latter only for NVFP4 whose weights
 are exact in bf16), which stays inside that bound; accumulation is fp32.
-Shapes cover single tokens, ragged token and row tiles, several K steps and
-the Llama-8B prefill shapes (sampled outputs there).
+Shapes cover single tokens, ragged token and row tiles (256 tokens x 128 rows
+per workgroup), odd and even K step counts, split and unsplit K and the
+Llama-8B prefill shapes (sampled outputs there).
 """
 import numpy as np
 import pytest
@@ -51,6 +52,12 @@ CASES = [
     ("tq1", 131, 77, 1280, None, None),
     ("tq1", 512, 4096, 14336, 24, 200),
     ("tq1", 512, 14336, 4096, 24, 300),
+    # one past a 256-token tile and a 128-row tile; an odd step count (a zero step at the end)
+    ("q4k", 257, 129, 1280, None, None),
+    ("nvfp4", 300, 130, 192, None, None),
+    ("tq1", 256, 256, 768, None, None),
+    # many tiles, no K split
+    ("q4k", 2048, 4096, 4096, 24, 200),
 ]
 
 
