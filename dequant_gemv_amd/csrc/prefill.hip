@@ -4,16 +4,18 @@
 // dequantised a block at a time into a tile that a matrix unit consumes.
 //
 // Unlike the batch-1 GEMV this is a dense contraction (2 T flops per weight),
-// so it runs on MFMA: v_mfma_f32_16x16x32_{f16,bf16}, whose lane layout
-// (checked on the part) is A[m][k] at lane m%16 + 16 (k/8) element k%8,
-// B[k][n] at lane n%16 + 16 (k/8) element k%8, D[m][n] at lane n + 16 (m/4)
-// register m%4 (m, n < 16, k < 32).  Tokens are the MFMA's M, weight rows its
-// N, so a B fragment is 8 consecutive weights of one weight row.
+// so it runs on MFMA: v_mfma_f32_32x32x16_{f16,bf16}, whose lane layout
+// (checked on the part) is A[m][k] at lane m + 32 (k/8) element k%8, B[k][n]
+// at lane n + 32 (k/8) element k%8, D[m][n] at lane n + 32 ((m/4) % 2)
+// register 4 (m/8) + m%4 (m, n < 32, k < 16).  Tokens are the MFMA's M,
+// weight rows its N, so a B fragment is 8 consecutive weights of one weight
+// row.  (This shape sustains about 78% of the unit's peak from one wave per
+// SIMD on the part, 16x16x32 about half.)
 //
 // Work split.  A workgroup of 8 waves (two per SIMD: one wave per SIMD
 // issues these MFMAs at about half the unit's rate) owns a tile of 256 tokens
 // x 128 weight rows and walks K in steps of 64 weights; each wave accumulates
-// a 64 x 64 sub-tile (4 x 4 MFMA tiles).  Per step:
+// a 64 x 64 sub-tile (2 x 2 MFMA tiles of 32 x 32).  Per step:
 //  - the activations of the tile (256 x 64 values, 32 KiB) go straight from
 //    global memory into LDS (buffer loads with the LDS bit, no registers);
 //    row t's 16-byte granule g sits at position g ^ (t & 7) of its 128-byte
@@ -22,7 +24,7 @@
 //    format's functor: packed bytes straight from global memory into
 //    registers, one rounding to the MFMA input type) and writes them to LDS
 //    with the same swizzle;
-//  - each wave reads 16 A and B fragments (ds_read_b128) and issues 32 MFMAs.
+//  - each wave reads 16 A and B fragments (ds_read_b128) and issues 16 MFMAs.
 // Each packed weight is decoded once per 256 tokens.
 
 #include "device.hpp"
@@ -32,7 +34,7 @@ namespace qgemv {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPfBT = 256;    // tokens per workgroup tile
 constexpr int kPfBN = 128;    // weight rows per workgroup tile
@@ -49,6 +51,24 @@ constexpr uint32_t kPfDead = 0x80000000u;
 
 // LDS byte offset of 16-byte granule g (0..7) of tile row t.
 __device__ __forceinline__ int pf_off(int t, int g) { return t * kPfRowB + 16 * (g ^ (t & 7)); }
+
+// fp16 pair (fma(a_H, s, m), fma(b_H, s, m)), each rounded once from the
+// exact value, where a_H, b_H are the fp16 values in half H of a and b:
+// v_fma_mix reads an fp16 operand from either half of a register and writes
+// either half of the result (the compiler forms the low write but packs the
+// high one with a shift and an or).
+template <int H>
+__device__ __forceinline__ unsigned mix_pair(unsigned a, unsigned b, float s, float m, Int<H>) {
+  unsigned d;
+  if constexpr (H == 0) {
+    __asm__("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(a), "v"(s), "v"(m));
+    __asm__("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "+v"(d) : "v"(b), "v"(s), "v"(m));
+  } else {
+    __asm__("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(a), "v"(s), "v"(m));
+    __asm__("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(d) : "v"(b), "v"(s), "v"(m));
+  }
+  return d;
+}
 
 // Two fp32 values -> two 16-bit codes of T (round to nearest even), packed.
 template <typename T>
@@ -96,7 +116,11 @@ struct Q4kPrefill {
     raw.qs = ld128s(d.r, ro + 16u * (uint32_t)(q & 1), so + 16u + 32u * (uint32_t)(s & 3));
     return raw;
   }
-  // weight = d * scale * q - dmin * min, rounded once from fp32
+  // weight = d * scale * q - dmin * min, rounded once from the exact value to
+  // fp16: a nibble masked in place is the fp16 subnormal q * 2^-24 (low
+  // nibble) or q * 2^-20 (high nibble), exact, and one mixed-precision fma
+  // (v_fma_mix) multiplies it by the fp32 d * scale * 2^24 (or 2^20), adds
+  // -dmin * min and rounds once to fp16.
   static __device__ __forceinline__ void make(const Raw& raw, int s, int q, unsigned (&out)[8]) {
     const int c = s & 3;
     const unsigned h = (unsigned)q >> 1;
@@ -107,18 +131,17 @@ struct Q4kPrefill {
     const unsigned sa = hi ? raw.hdr.w : raw.hdr.y, mb = hi ? raw.hdr.w : raw.hdr.z;
     const unsigned sg = ((sa >> sh) & ma) | (hi ? (((raw.hdr.y >> (sh + 6)) & 3u) << 4) : 0u);
     const unsigned mg = ((mb >> (sh + (hi ? 4u : 0u))) & ma) | (hi ? (((raw.hdr.z >> (sh + 6)) & 3u) << 4) : 0u);
-    const float ds = f16lo(raw.hdr.x) * (float)sg, dm = f16hi(raw.hdr.x) * (float)mg;
+    // d * scale (exact in fp32: 11 x 6 significant bits) times 2^24 / 2^20
+    const float ds = f16lo(raw.hdr.x) * (float)sg * (h ? 1048576.f : 16777216.f);
+    const float ndm = -(f16hi(raw.hdr.x) * (float)mg);
+    const unsigned mask = h ? 0x00F000F0u : 0x000F000Fu;
     const unsigned qw[4] = {raw.qs.x, raw.qs.y, raw.qs.z, raw.qs.w};
-    const unsigned nsh = 4u * h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const unsigned v = (qw[i] >> nsh) & 0x0F0F0F0Fu;  // four nibbles, one per byte
-      const float w0 = __builtin_fmaf(ds, (float)(v & 0xFFu), -dm);
-      const float w1 = __builtin_fmaf(ds, (float)((v >> 8) & 0xFFu), -dm);
-      const float w2 = __builtin_fmaf(ds, (float)((v >> 16) & 0xFFu), -dm);
-      const float w3 = __builtin_fmaf(ds, (float)(v >> 24), -dm);
-      out[2 * i] = pf_pack2<T>(w0, w1);
-      out[2 * i + 1] = pf_pack2<T>(w2, w3);
+      const unsigned a = qw[i] & mask;         // elements 4i, 4i + 2 of the 16
+      const unsigned b = (qw[i] >> 8) & mask;  // elements 4i + 1, 4i + 3
+      out[2 * i] = mix_pair(a, b, ds, ndm, Int<0>{});
+      out[2 * i + 1] = mix_pair(a, b, ds, ndm, Int<1>{});
     }
   }
 };
@@ -241,7 +264,7 @@ struct Tq1Prefill {
 #define QGEMV_PREFILL_INTERLEAVE 0  // ALU instructions placed after each MFMA (0: the compiler's order)
 #endif
 #ifndef QGEMV_PREFILL_XSTAGES
-#define QGEMV_PREFILL_XSTAGES 2  // activation stages in LDS (2 or 3)
+#define QGEMV_PREFILL_XSTAGES 3  // activation stages in LDS (2 or 3)
 #endif
 constexpr int kPfXS = QGEMV_PREFILL_XSTAGES;
 static_assert(kPfXS == 2 || kPfXS == 3, "two or three activation stages");
@@ -303,15 +326,17 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
       *reinterpret_cast<u32x4*>(stage + pf_off(dr, 2 * dq + g)) = u32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
   };
 
-  f32x4 acc[4][4];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // wave sub-tile: tokens 64 (wave & 3) .., rows 64 (wave >> 2) ..
   const int wt = 64 * (wave & 3), wn = 64 * (wave >> 2);
-  const int fl = lane & 15, fq = lane >> 4;  // fragment row / column and k-granule
+  const int fl = lane & 31, fq = lane >> 5;  // fragment row / column and k-granule
   auto xstage = [&](int m) { return m % kPfXS == 0 ? xs0 : m % kPfXS == 1 ? xs1 : xs2; };
 
   // Loads return in issue order, and the wait counts below count the loads
@@ -363,23 +388,23 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
       unsigned v[8];
       F::make(wq[(I + 1) % 2], s_begin + s + 1, dq, v);
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int g = 4 * kh + fq;
-        u32x4 af[4], bf[4];
+      for (int kc = 0; kc < 4; ++kc) {  // 16 weights of K per MFMA
+        const int g = 2 * kc + fq;
+        u32x4 af[2], bf[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4*>(xa + pf_off(wt + 16 * i + fl, g));
+        for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const u32x4*>(xa + pf_off(wt + 32 * i + fl, g));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(wa + pf_off(wn + 16 * j + fl, g));
+        for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const u32x4*>(wa + pf_off(wn + 32 * j + fl, g));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < 2; ++j) {
             if constexpr (F::kBf16)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
                                                                    __builtin_bit_cast(bf16x8, bf[j]), acc[i][j],
                                                                    0, 0, 0);
             else
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, af[i]),
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, af[i]),
                                                                   __builtin_bit_cast(half8, bf[j]), acc[i][j], 0,
                                                                   0, 0);
           }
@@ -389,9 +414,9 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
       // issue order: each half-step's fragment reads, then each MFMA followed
       // by a few of the decode's ALU instructions (in-order issue would
       // otherwise run them all after the last MFMA)
-      static_for<0, 2>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x0100, 8, 0);  // 8 DS reads
-        static_for<0, 16>([&](auto) {
+      static_for<0, 4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // 4 DS reads
+        static_for<0, 4>([&](auto) {
           __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // 1 MFMA
           __builtin_amdgcn_sched_group_barrier(0x0002, QGEMV_PREFILL_INTERLEAVE, 0);  // VALU
         });
@@ -402,22 +427,23 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
     });
   }
 
-  // D[m][n] of tile (i, j) sits at lane n + 16 (m / 4), register m % 4
+  // D[m][n] of tile (i, j) sits at lane n + 32 ((m / 4) % 2), register
+  // 4 (m / 8) + m % 4: register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int t = t0 + wt + 16 * i + 4 * fq + a;
+    for (int r = 0; r < 16; ++r) {
+      const int t = t0 + wt + 32 * i + 8 * (r >> 2) + 4 * fq + (r & 3);
       if (t < t_count) {
         float* const yr = y + (int64_t)t * n;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn + 16 * j + fl;
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn + 32 * j + fl;
           if (col < n) {
             if (gridDim.z == 1)
-              yr[col] = acc[i][j][a];
+              yr[col] = acc[i][j][r];
             else
-              atomicAdd(yr + col, acc[i][j][a]);  // partial sum of one K split (y zeroed first)
+              atomicAdd(yr + col, acc[i][j][r]);  // partial sum of one K split (y zeroed first)
           }
         }
       }
