@@ -17,14 +17,17 @@
 // are zero, the zero-padding trick of the page's section 1, so all byte pairs
 // run one code path.
 //
-// Digits in registers: with B = (b0 | b1 << 16) and packed 16-bit arithmetic
-// (wrapping mod 2^16), F_k = (B * 4 * 3^k) & 0xFC00 = floor(3^k b / 256) << 10
-// (mod 2^16), and F_{k+1} - 3 F_k = digit_k << 10 exactly.  The 16-bit pattern
-// digit << 10 is the fp16 number digit * 2^-14 (0, 2^-14 or 2^-13, all normal
-// or zero), so v_dot2_f32_f16 consumes it directly against the activation pair:
-// sum x*t = 2^14 * acc exactly up to fp32 accumulation.  No fp16 arithmetic
-// touches the digits themselves (the page's "Not applicable" section shows why
-// fp16 floors fail).
+// Digits in registers: with L_0 = b and L_{k+1} = 3 L_k mod 256 (the
+// fractional part of 3^(k+1) b / 256, in 256ths), digit k is floor(3 L_k /
+// 256), because 3^(k+1) b = 3 (256 floor(3^k b / 256) + L_k).  With B = (b0 |
+// b1 << 16) both bytes go through one 32-bit multiply by 3 (each half stays
+// below 768, so no carry crosses) and two masks per digit: 3 L & 0xFF00FF00
+// holds digit << 8 in each half, 3 L & 0x00FF00FF the next L.  The 16-bit
+// pattern digit << 8 is the fp16 subnormal digit * 2^-16 (exact), so
+// v_dot2_f32_f16 consumes it directly against the activation pair: sum x*t =
+// 2^16 * acc exactly up to fp32 accumulation.  No fp16 arithmetic touches the
+// digits themselves (the page's "Not applicable" section shows why fp16
+// floors fail).
 //
 // Each block's d sits in the lane whose 16 bytes hold bytes 52-53 of that
 // block; lanes fetch the d of the (at most two) blocks they touch with
@@ -56,24 +59,17 @@ __device__ __forceinline__ int tq1_element(int pos, int k) {
   return -1;
 }
 
-typedef __attribute__((ext_vector_type(2))) unsigned short u16v2;
 
-__device__ __forceinline__ u16v2 as_u16v2(unsigned v) { return __builtin_bit_cast(u16v2, v); }
-__device__ __forceinline__ unsigned as_u32(u16v2 v) { return __builtin_bit_cast(unsigned, v); }
-
-// Five fp16 pairs (digit_k(b0) * 2^-14, digit_k(b1) * 2^-14), k = 0..4.
+// Five fp16 pairs (digit_k(b0) * 2^-16, digit_k(b1) * 2^-16), k = 0..4, from
+// B = b0 | b1 << 16 (32-bit operations, cheaper here than packed 16-bit ones).
 __device__ __forceinline__ void tq1_digits(unsigned B, unsigned (&D)[5]) {
-  const u16v2 b = as_u16v2(B);
-  const u16v2 m = {0xFC00, 0xFC00};
-  u16v2 F[6];
+  unsigned L = B;
 #pragma unroll
-  for (int k = 1; k <= 5; ++k) {
-    const unsigned short c = (unsigned short)(4 * (k == 1 ? 3 : k == 2 ? 9 : k == 3 ? 27 : k == 4 ? 81 : 243));
-    F[k] = (b * (u16v2){c, c}) & m;
+  for (int k = 0; k < 5; ++k) {
+    const unsigned t = L * 3u;  // 3 L_k per half, < 768
+    D[k] = t & 0xFF00FF00u;     // digit_k << 8 per half
+    L = t & 0x00FF00FFu;        // L_{k+1}
   }
-  D[0] = as_u32(F[1]);
-#pragma unroll
-  for (int k = 1; k <= 4; ++k) D[k] = as_u32(F[k + 1] + F[k] * (u16v2){0xFFFD, 0xFFFD});
 }
 
 template <int R, typename Out>
@@ -172,8 +168,8 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void tq1_gemv_kernel(const uin
         for (int k = 0; k < 5; ++k) a = dot2h(D[k], xp[i][k], a);
         snap = (i == bnd - 1) ? a : snap;
       }
-      float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0), acc[r]);
-      acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1), t);
+      float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 65536.f, -xs0), acc[r]);
+      acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 65536.f, -xs1), t);
     }
   }
 
@@ -329,8 +325,8 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
       for (int k = 0; k < 5; ++k) a = dot2h(D[k], xp[sg][i][k], a);
       snap = last_of_first[i] ? a : snap;
     }
-    const float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 16384.f, -xs0[sg]), acc[r]);
-    acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 16384.f, -xs1[sg]), t);
+    const float t = __builtin_fmaf(d0, __builtin_fmaf(snap, 65536.f, -xs0[sg]), acc[r]);
+    acc[r] = __builtin_fmaf(d1, __builtin_fmaf(a - snap, 65536.f, -xs1[sg]), t);
   });
   store_rows<R>(acc, out, pre, row0, nrows, 1.f, lane);
 }
