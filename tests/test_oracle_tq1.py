@@ -44,6 +44,23 @@ def test_digits_are_base3_of_scaled_byte():
         assert [oracle.tq1_digit(b, k) for k in range(5)] == want
 
 
+def test_packed_digit_recurrence_all_byte_pairs():
+    # The GEMV's digit arithmetic: both bytes of a pair in one 32-bit word,
+    # L_0 = b, t = 3 L_k, digit_k << 8 = t & 0xFF00 per 16-bit half, L_{k+1} =
+    # t & 0xFF; checked against the oracle's digit for every byte pair (no
+    # carry may cross between the halves).
+    b0 = np.repeat(np.arange(256, dtype=np.uint64), 256)
+    b1 = np.tile(np.arange(256, dtype=np.uint64), 256)
+    L = b0 | (b1 << np.uint64(16))
+    want = np.array([[oracle.tq1_digit(b, k) for k in range(5)] for b in range(256)], dtype=np.uint64)
+    for k in range(5):
+        t = (L * np.uint64(3)) & np.uint64(0xFFFFFFFF)
+        d = t & np.uint64(0xFF00FF00)
+        assert np.array_equal(d & np.uint64(0xFFFF), want[b0.astype(np.int64), k] << np.uint64(8)), k
+        assert np.array_equal(d >> np.uint64(16), want[b1.astype(np.int64), k] << np.uint64(8)), k
+        L = t & np.uint64(0x00FF00FF)
+
+
 def test_collapse_identity_all_bytes_exact():
     rng = np.random.default_rng(7)
     for b in range(256):
