@@ -183,6 +183,11 @@ def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
 LLAMA8B_LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
                  ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
 LLAMA8B_HEAD = ("lm_head", 128256, 4096)
+# The same layer with the GEMVs that share an activation row stored as one
+# matrix (Q, K, V rows concatenated; gate and up rows concatenated): 4 launches
+# per layer instead of 7, the same weight bytes.
+LLAMA8B_LAYER_FUSED = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)]
+FUSED_ROLE_OF = {"qkv": "q", "gate_up": "gate"}
 SWEEP_MIXES = {
     # attention and lm_head Q4_K, gate/up TQ1_0, down NVFP4
     "mixed": {"q": "q4k", "k": "q4k", "v": "q4k", "o": "q4k", "gate": "tq1", "up": "tq1",
@@ -195,16 +200,22 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
     """One token = the 225 GEMVs of a Llama-8B decode step, each layer with its
     own weight buffers (cloned on the device from one generated matrix per
     shape, so every launch reads cold bytes: ~2.9 GB for the mixed sweep),
-    captured in one HIP graph and replayed per token."""
+    captured in one HIP graph and replayed per token.  A mix named "<mix>-fused"
+    stores Q/K/V and gate/up as concatenated matrices (129 launches)."""
     import numpy as np
     import torch
 
     from dequant_gemv_amd import qgemv, synth
 
     dev = torch.device("cuda:0")
-    fmt_of = SWEEP_MIXES[mix] or {r: mix for r, _, _ in LLAMA8B_LAYER + [LLAMA8B_HEAD]}
+    fused = mix.endswith("-fused")
+    mix = mix[: -len("-fused")] if fused else mix
+    layer_shapes = LLAMA8B_LAYER_FUSED if fused else LLAMA8B_LAYER
+    fmt_of = dict(SWEEP_MIXES[mix] or {r: mix for r, _, _ in LLAMA8B_LAYER + [LLAMA8B_HEAD]})
+    for role, base in FUSED_ROLE_OF.items():
+        fmt_of[role] = fmt_of[base]
     proto, xs = {}, {}
-    for role, n, k in LLAMA8B_LAYER + [LLAMA8B_HEAD]:
+    for role, n, k in layer_shapes + [LLAMA8B_HEAD]:
         fmt = fmt_of[role]
         key = (fmt, n, k)
         if key not in proto:
@@ -213,7 +224,7 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
             xs[key] = torch.from_numpy(synth.activations(fmt, k, seed + 1).view(np.int16).copy()).to(dev)
     calls, total_bytes = [], 0
     for layer in range(layers):
-        for role, n, k in LLAMA8B_LAYER:
+        for role, n, k in layer_shapes:
             fmt = fmt_of[role]
             w = proto[(fmt, n, k)].clone()
             calls.append((fmt, w, xs[(fmt, n, k)], torch.empty(n, dtype=torch.float32, device=dev), n, k))
@@ -249,7 +260,8 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
     torch.cuda.synchronize()
     us = 1e3 * ev0.elapsed_time(ev1) / tokens
     res = {
-        "workload": f"Llama-8B decode step, {len(calls)} GEMVs ({layers} layers + lm_head), formats: {mix}",
+        "workload": f"Llama-8B decode step, {len(calls)} GEMVs ({layers} layers + lm_head), formats: {mix}"
+                    + (", Q/K/V and gate/up as concatenated matrices" if fused else ""),
         "gemvs_per_token": len(calls),
         "algorithmic_bytes_per_token": total_bytes,
         "us_per_token": round(us, 2),
@@ -486,8 +498,9 @@ def main():
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-extra", action="store_true", help="skip the other formats' shapes")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--sweep", default="mixed",
-                    help="Llama-8B per-token sweep(s) to time among mixed,q4k,nvfp4,tq1 (comma list; 'none' to skip)")
+    ap.add_argument("--sweep", default="mixed,mixed-fused",
+                    help="Llama-8B per-token sweep(s) to time among mixed,q4k,nvfp4,tq1, each also as "
+                         "<mix>-fused (comma list; 'none' to skip)")
     ap.add_argument("--sweep-tokens", type=int, default=20)
     ap.add_argument("--fmt", default=None, help="measure only this format (q4k, nvfp4, tq1, f16, bf16) at N,K")
     ap.add_argument("--n", type=int, default=None)

@@ -170,6 +170,8 @@ FULL = [
     ("nvfp4", 4096, 14336, 2), ("tq1", 14336, 4096, 3),
     # Llama-8B attention K/V projection and lm_head rows
     ("q4k", 1024, 4096, 4), ("nvfp4", 1024, 4096, 4), ("tq1", 1024, 4096, 4),
+    # the concatenated Q/K/V and gate/up matrices of the fused decode sweep
+    ("q4k", 6144, 4096, 5), ("tq1", 28672, 4096, 5),
 ]
 
 
