@@ -268,13 +268,15 @@ struct Tq1Prefill {
 #endif
 constexpr int kPfXS = QGEMV_PREFILL_XSTAGES;
 static_assert(kPfXS == 2 || kPfXS == 3, "two or three activation stages");
-constexpr int kPfUnroll = kPfXS == 3 ? 6 : 2;  // steps per loop iteration: stage indices are compile-time
+constexpr int kPfWQ = 3;      // packed-weight register slots: loads run kPfWQ - 1 steps ahead of the decode
+constexpr int kPfUnroll = 6;  // steps per loop iteration (a multiple of XS, 2 and kPfWQ): indices are compile-time
 
 // Step s, with XS activation stages: the activations of step s + XS - 1 are
 // copied into activation stage (s + XS - 1) % XS and the packed weights of
-// step s + 2 are loaded into registers; the MFMAs consume activation stage
-// s % XS and weight stage s % 2; then the weights of step s + 1 (loaded
-// during step s - 1) are decoded and written to weight stage (s + 1) % 2.
+// step s + 3 are loaded into registers; the weights of step s + 1 (loaded
+// during step s - 2) are decoded, the MFMAs consume activation stage s % XS
+// and weight stage s % 2, and the decoded weights go to weight stage
+// (s + 1) % 2.
 // Before the step's barrier each wave waits for its own copy of step s + 1's
 // activations (an LDS copy by one wave is read by all), so every copy has
 // XS - 1 steps to land.  The stages are separate LDS arrays indexed at
@@ -343,11 +345,11 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
   // issued after the one waited for: per step the activation copy (4), then
   // the weights (kLoads).
   constexpr int kStepLoads = 4 + F::kLoads;
-  // prologue: activations of steps 0 .. XS - 2, weights of steps 0 and 1; step 0 decoded
+  // prologue: activations of steps 0 .. XS - 2, weights of steps 0 .. 2; step 0 decoded
   // Each group is fenced: the compiler may otherwise interleave independent
   // loads, and a weight load issued after a copy would let part of the copy
   // still be in flight when the count is reached.
-  typename F::Raw wq[2];
+  typename F::Raw wq[kPfWQ];
   copy_x(xs0, 0);
   compiler_fence();
   wq[0] = F::load(wd, dr, s_begin, dq, 0 < steps);
@@ -358,12 +360,16 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
   }
   wq[1] = F::load(wd, dr, s_begin + 1, dq, 1 < steps);
   compiler_fence();
+  wq[2] = F::load(wd, dr, s_begin + 2, dq, 2 < steps);
+  compiler_fence();
   {
     unsigned v[8];
     F::make(wq[0], s_begin, dq, v);
     store_w(ws0, v);
   }
-  wait_vm<kPfXS == 3 ? kStepLoads : F::kLoads>();  // this wave's copy of step 0's activations
+  // this wave's copy of step 0's activations (what may still be in flight:
+  // the copy of step 1 and the weights of steps 1 and 2)
+  wait_vm<(kPfXS == 3 ? 4 : 0) + 2 * F::kLoads>();
   lds_barrier();
 
   // Every iteration runs kPfUnroll steps with no branch between them (a
@@ -380,13 +386,13 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
       unsigned char* const wb = I % 2 ? ws0 : ws1;  // filled for step s + 1
       copy_x(xc, s + kPfXS - 1);
       compiler_fence();
-      wq[I % 2] = F::load(wd, dr, s_begin + s + 2, dq, s + 2 < steps);
+      wq[I % kPfWQ] = F::load(wd, dr, s_begin + s + kPfWQ, dq, s + kPfWQ < steps);
       compiler_fence();
       // (no decode arithmetic above the loads: it would wait for step s + 1's
       // weights before this step's loads are even issued)
       __builtin_amdgcn_sched_barrier(0);
       unsigned v[8];
-      F::make(wq[(I + 1) % 2], s_begin + s + 1, dq, v);
+      F::make(wq[(I + 1) % kPfWQ], s_begin + s + 1, dq, v);
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {  // 16 weights of K per MFMA
         const int g = 2 * kc + fq;
