@@ -260,9 +260,6 @@ struct Tq1Prefill {
 
 // ---- the kernel ---------------------------------------------------------------
 
-#ifndef QGEMV_PREFILL_INTERLEAVE
-#define QGEMV_PREFILL_INTERLEAVE 0  // ALU instructions placed after each MFMA (0: the compiler's order)
-#endif
 #ifndef QGEMV_PREFILL_XSTAGES
 #define QGEMV_PREFILL_XSTAGES 3  // activation stages in LDS (2 or 3)
 #endif
@@ -416,18 +413,6 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
           }
       }
       store_w(wb, v);
-#if QGEMV_PREFILL_INTERLEAVE
-      // issue order: each half-step's fragment reads, then each MFMA followed
-      // by a few of the decode's ALU instructions (in-order issue would
-      // otherwise run them all after the last MFMA)
-      static_for<0, 4>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // 4 DS reads
-        static_for<0, 4>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x0002, QGEMV_PREFILL_INTERLEAVE, 0);  // VALU
-        });
-      });
-#endif
       wait_vm<(kPfXS - 2) * kStepLoads + F::kLoads>();  // this wave's copy of step s + 1's activations
       lds_barrier();  // all reads of this step's stages and all writes of the next are done
     });
