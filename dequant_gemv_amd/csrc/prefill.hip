@@ -12,9 +12,9 @@
 // row.  (This shape sustains about 78% of the unit's peak from one wave per
 // SIMD on the part, 16x16x32 about half.)
 //
-// Work split.  A workgroup of 8 waves (two per SIMD: one wave per SIMD
-// issues these MFMAs at about half the unit's rate) owns a tile of 256 tokens
-// x 128 weight rows and walks K in steps of 64 weights; each wave accumulates
+// Work split.  A workgroup of 8 waves (two per SIMD, so that one wave's
+// loads, decode and barrier waits overlap the other's MFMAs) owns a tile of
+// 256 tokens x 128 weight rows and walks K in steps of 64 weights; each wave accumulates
 // a 64 x 64 sub-tile (2 x 2 MFMA tiles of 32 x 32).  Per step:
 //  - the activations of the tile (256 x 64 values, 32 KiB) go straight from
 //    global memory into LDS (buffer loads with the LDS bit, no registers);
