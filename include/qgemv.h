@@ -148,8 +148,12 @@ int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int6
  * [T][M] row-major fp32.  W, M and K as for the GEMV of the same format, plus
  * K <= 2^21 and T <= 65535 * 128.  The weights are dequantised to the
  * activation type (one rounding per weight) and multiplied on the matrix
- * cores with fp32 accumulation.  T == 0 or M == 0 is a successful no-op; y
- * must not overlap W or x. */
+ * cores with fp32 accumulation.  Every element of y is overwritten.  When the
+ * output has few 256 x 128 tiles the K range is split across workgroups whose
+ * partial sums are added into y with fp32 atomics (after y is cleared on the
+ * same stream), so the last bits can differ from run to run; the error bound
+ * is unchanged.  T == 0 or M == 0 is a successful no-op; y must not overlap W
+ * or x. */
 int qgemm_q4k(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
               struct ihipStream_t* stream);
 /* NVFP4 prefill: x is [T][K] bf16; K % 64 == 0.  The weights e2m1 * |scale|
@@ -157,8 +161,8 @@ int qgemm_q4k(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, 
 int qgemm_nvfp4(const void* w, const void* x_bf16, float* y, int64_t T, int64_t M, int64_t K,
                 struct ihipStream_t* stream);
 /* TQ1_0 prefill: x is [T][K] fp16.  The weights d * (t - 1) are exact in
- * fp16 ("metal: TQ1_0 kernel performance", section "Prefill": the block is
- * unpacked a whole 64-weight step at a time). */
+ * fp16 ("metal: TQ1_0 kernel performance", section "Prefill": blocks are
+ * unpacked into a tile that the matrix unit reads). */
 int qgemm_tq1(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
               struct ihipStream_t* stream);
 
