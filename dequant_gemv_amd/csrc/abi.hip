@@ -134,9 +134,8 @@ int get_rows(Fmt f, const void* w, int64_t m, int64_t k, const int32_t* rows, in
 int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, int64_t k, hipStream_t s) {
   int rc = check_shape(f, m, k);
   if (rc != QGEMV_OK) return rc;
-  // the grid's y dimension counts tiles of 256 activation rows (at most
-  // 65535; this bound keeps it at half that); an activation tile spans
-  // 256 * 2K < 2^31 bytes
+  // the grid's y dimension counts tiles of 256 or 512 activation rows (at
+  // most 65535); an activation tile spans at most 512 * 2K <= 2^30 bytes
   if (t < 0 || t > 65535 * int64_t(128) || k > qgemv::kPrefillMaxK) return QGEMV_E_SHAPE;
   if (f == kNvfp4 && k % 64 != 0) return QGEMV_E_SHAPE;  // whole 64-weight steps
   if (t == 0 || m == 0) return QGEMV_OK;

@@ -32,7 +32,7 @@ hipError_t launch_nvfp4_get_rows(const void* w, int64_t n, int64_t k, const int3
 hipError_t launch_tq1_get_rows(const void* w, int64_t n, int64_t k, const int32_t* rows, int64_t nrows, void* out,
                                int dtype, hipStream_t s);
 // Prefill: y[t][r] (fp32, [T][n]) = x[t] . dequant(W)[r] for T activation rows.
-constexpr int64_t kPrefillMaxK = int64_t(1) << 21;
+constexpr int64_t kPrefillMaxK = int64_t(1) << 20;
 hipError_t launch_q4k_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s);
 hipError_t launch_nvfp4_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
                                 hipStream_t s);

@@ -14,9 +14,10 @@
 //
 // Work split.  A workgroup of 8 waves (two per SIMD, so that one wave's
 // loads, decode and barrier waits overlap the other's MFMAs) owns a tile of
-// 256 tokens x 128 weight rows and walks K in steps of 64 weights; each wave accumulates
-// a 64 x 64 sub-tile (2 x 2 MFMA tiles of 32 x 32).  Per step:
-//  - the activations of the tile (256 x 64 values, 32 KiB) go straight from
+// BT = 256 or 512 tokens x 128 weight rows and walks K in steps of 64
+// weights; each wave accumulates a BT/4 x 64 sub-tile (BT/128 x 2 MFMA tiles
+// of 32 x 32).  Per step:
+//  - the activations of the tile (BT x 64 values, 32 or 64 KiB) go straight from
 //    global memory into LDS (buffer loads with the LDS bit, no registers);
 //    row t's 16-byte granule g sits at position g ^ (t & 7) of its 128-byte
 //    LDS row, so that the lanes of a fragment read hit different banks;
@@ -25,7 +26,7 @@
 //    registers, one rounding to the MFMA input type) and writes them to LDS
 //    with the same swizzle;
 //  - each wave reads 16 A and B fragments (ds_read_b128) and issues 16 MFMAs.
-// Each packed weight is decoded once per 256 tokens.
+// Each packed weight is decoded once per BT tokens.
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -36,11 +37,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPfBT = 256;    // tokens per workgroup tile
 constexpr int kPfBN = 128;    // weight rows per workgroup tile
 constexpr int kPfKS = 64;     // weights per K step
 constexpr int kPfRowB = 128;  // LDS bytes per tile row per step (64 16-bit values)
-constexpr int kPfXTile = kPfBT * kPfRowB;  // 32 KiB of activations per stage
 constexpr int kPfWTile = kPfBN * kPfRowB;  // 16 KiB of weights per stage
 constexpr int kPfWaves = 8;
 
@@ -260,11 +259,6 @@ struct Tq1Prefill {
 
 // ---- the kernel ---------------------------------------------------------------
 
-#ifndef QGEMV_PREFILL_XSTAGES
-#define QGEMV_PREFILL_XSTAGES 3  // activation stages in LDS (2 or 3)
-#endif
-constexpr int kPfXS = QGEMV_PREFILL_XSTAGES;
-static_assert(kPfXS == 2 || kPfXS == 3, "two or three activation stages");
 constexpr int kPfWQ = 3;      // packed-weight register slots: loads run kPfWQ - 1 steps ahead of the decode
 constexpr int kPfUnroll = 6;  // steps per loop iteration (a multiple of XS, 2 and kPfWQ): indices are compile-time
 
@@ -280,11 +274,18 @@ constexpr int kPfUnroll = 6;  // steps per loop iteration (a multiple of XS, 2 a
 // compile time (the loop runs kPfUnroll steps per iteration): the compiler
 // then knows that the copies in flight into one stage never alias the
 // fragment reads of another, and does not wait for them there.
-template <typename F>
+template <typename F, int BT>
 __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t* __restrict__ w,
                                                                   const uint16_t* __restrict__ x,
                                                                   float* __restrict__ y, int t_count, int n,
                                                                   int k, int split_steps) {
+  static_assert(BT == 256 || BT == 512, "256 or 512 tokens per tile");
+  constexpr int kPfBT = BT;                       // tokens per workgroup tile
+  constexpr int kPfXTile = BT * kPfRowB;          // 32 or 64 KiB of activations per stage
+  constexpr int kPfXS = BT == 512 ? 2 : 3;        // activation stages (as many as fit the LDS)
+  constexpr int kPfMI = BT / 128;                 // 32-token MFMA tiles per wave (waves are 4 x 2)
+  constexpr int kPfCopies = BT / 64;              // 1 KiB activation copies per wave per step
+  static_assert(kPfXS * kPfXTile + 2 * kPfWTile <= 160 * 1024, "activation and weight stages fit the LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[kPfXTile];
   __shared__ __attribute__((aligned(1024))) unsigned char xs1[kPfXTile];
   __shared__ __attribute__((aligned(1024))) unsigned char xs2[kPfXS == 3 ? kPfXTile : 16];
@@ -304,16 +305,17 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
   const auto xr = make_rsrc(x + (int64_t)t0 * k, (uint32_t)tv * xrow);
   const typename F::Desc wd = F::desc(w, n, k, n0, nv);
 
-  // Activation copy: wave v copies tile rows 32 v .. 32 v + 31 of a step in 4
-  // wave-wide loads of 8 rows; lane i of load j lands at LDS row 32 v + 8 j +
-  // i / 8, position i % 8, which holds granule (i % 8) ^ (i / 8) of the row.
+  // Activation copy: wave v copies tile rows 8C v .. 8C v + 8C - 1 of a step
+  // in C = kPfCopies wave-wide loads of 8 rows; lane i of load j lands at LDS
+  // row 8C v + 8 j + i / 8, position i % 8, which holds granule (i % 8) ^
+  // (i / 8) of the row.
   const uint32_t xlane =
-      (uint32_t)(32 * wave + (lane >> 3)) * xrow + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+      (uint32_t)(8 * kPfCopies * wave + (lane >> 3)) * xrow + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
   auto copy_x = [&](unsigned char* stage, int s) {
     const uint32_t so = s < steps ? (uint32_t)(s_begin + s) * 128u : kPfDead;  // uniform
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      ld128_lds_s(xr, stage + (32 * wave + 8 * j) * kPfRowB, xlane, so + (uint32_t)j * 8u * xrow);
+    for (int j = 0; j < kPfCopies; ++j)
+      ld128_lds_s(xr, stage + (8 * kPfCopies * wave + 8 * j) * kPfRowB, xlane, so + (uint32_t)j * 8u * xrow);
   };
 
   // Weight decode: thread i takes weights [16 dq, 16 dq + 16) of weight row
@@ -325,23 +327,23 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
       *reinterpret_cast<u32x4*>(stage + pf_off(dr, 2 * dq + g)) = u32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[kPfMI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kPfMI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // wave sub-tile: tokens 64 (wave & 3) .., rows 64 (wave >> 2) ..
-  const int wt = 64 * (wave & 3), wn = 64 * (wave >> 2);
+  // wave sub-tile: tokens 32 MI (wave & 3) .., rows 64 (wave >> 2) ..
+  const int wt = 32 * kPfMI * (wave & 3), wn = 64 * (wave >> 2);
   const int fl = lane & 31, fq = lane >> 5;  // fragment row / column and k-granule
   auto xstage = [&](int m) { return m % kPfXS == 0 ? xs0 : m % kPfXS == 1 ? xs1 : xs2; };
 
   // Loads return in issue order, and the wait counts below count the loads
   // issued after the one waited for: per step the activation copy (4), then
   // the weights (kLoads).
-  constexpr int kStepLoads = 4 + F::kLoads;
+  constexpr int kStepLoads = kPfCopies + F::kLoads;
   // prologue: activations of steps 0 .. XS - 2, weights of steps 0 .. 2; step 0 decoded
   // Each group is fenced: the compiler may otherwise interleave independent
   // loads, and a weight load issued after a copy would let part of the copy
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
   }
   // this wave's copy of step 0's activations (what may still be in flight:
   // the copy of step 1 and the weights of steps 1 and 2)
-  wait_vm<(kPfXS == 3 ? 4 : 0) + 2 * F::kLoads>();
+  wait_vm<(kPfXS == 3 ? kPfCopies : 0) + 2 * F::kLoads>();
   lds_barrier();
 
   // Every iteration runs kPfUnroll steps with no branch between them (a
@@ -393,13 +395,13 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {  // 16 weights of K per MFMA
         const int g = 2 * kc + fq;
-        u32x4 af[2], bf[2];
+        u32x4 af[kPfMI], bf[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const u32x4*>(xa + pf_off(wt + 32 * i + fl, g));
+        for (int i = 0; i < kPfMI; ++i) af[i] = *reinterpret_cast<const u32x4*>(xa + pf_off(wt + 32 * i + fl, g));
 #pragma unroll
         for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const u32x4*>(wa + pf_off(wn + 32 * j + fl, g));
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kPfMI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             if constexpr (F::kBf16)
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
   // D[m][n] of tile (i, j) sits at lane n + 32 ((m / 4) % 2), register
   // 4 (m / 8) + m % 4: register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kPfMI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = t0 + wt + 32 * i + 8 * (r >> 2) + 4 * fq + (r & 3);
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ y
   if (i < count) y[i] = 0.f;
 }
 
-// Tiles of 256 tokens x 128 rows, one workgroup per CU.  When there are
+// Tiles of 256 or 512 tokens x 128 rows, one workgroup per CU.  When there are
 // fewer tiles than CUs, K is split as well (one round of workgroups, at
 // least 8 steps per split) and the splits add their partial sums into y with
 // fp32 atomics, y being cleared by a fill kernel first (a kernel, so that the
@@ -455,7 +457,12 @@ __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ y
 template <typename F>
 static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
                                  hipStream_t s) {
-  const int64_t tiles = ((n + kPfBN - 1) / kPfBN) * ((t + kPfBT - 1) / kPfBT);
+  // 512-token tiles when they still fill at least two rounds of workgroups
+  // (each weight is then decoded half as often and each fragment read feeds
+  // more MFMAs), else 256-token tiles
+  const int64_t row_tiles = (n + kPfBN - 1) / kPfBN;
+  const int bt = row_tiles * ((t + 511) / 512) >= 512 ? 512 : 256;
+  const int64_t tiles = row_tiles * ((t + bt - 1) / bt);
   const int64_t steps = k / kPfKS;
   int64_t split = 1;
   if (tiles < 256) split = max(int64_t(1), 256 / tiles);  // fewer tiles than CUs
@@ -469,9 +476,13 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
     const int64_t count = t * n;
     hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, y, count);
   }
-  const dim3 grid((unsigned)((n + kPfBN - 1) / kPfBN), (unsigned)((t + kPfBT - 1) / kPfBT), (unsigned)split);
-  hipLaunchKernelGGL((prefill_kernel<F>), grid, dim3(64 * kPfWaves), 0, s, (const uint8_t*)w, (const uint16_t*)x,
-                     y, (int)t, (int)n, (int)k, (int)split_steps);
+  const dim3 grid((unsigned)row_tiles, (unsigned)((t + bt - 1) / bt), (unsigned)split);
+  if (bt == 512)
+    hipLaunchKernelGGL((prefill_kernel<F, 512>), grid, dim3(64 * kPfWaves), 0, s, (const uint8_t*)w,
+                       (const uint16_t*)x, y, (int)t, (int)n, (int)k, (int)split_steps);
+  else
+    hipLaunchKernelGGL((prefill_kernel<F, 256>), grid, dim3(64 * kPfWaves), 0, s, (const uint8_t*)w,
+                       (const uint16_t*)x, y, (int)t, (int)n, (int)k, (int)split_steps);
   return hipGetLastError();
 }
 

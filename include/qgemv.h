@@ -146,7 +146,7 @@ int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int6
  *     y[t][r] = sum_{i<K} x[t][i] * dequant(W)[r][i]     t < T, r < M
  * x is [T][K] row-major in the format's activation type (fp16 for Q4_K), y is
  * [T][M] row-major fp32.  W, M and K as for the GEMV of the same format, plus
- * K <= 2^21 and T <= 65535 * 128.  The weights are dequantised to the
+ * K <= 2^20 and T <= 65535 * 128.  The weights are dequantised to the
  * activation type (one rounding per weight) and multiplied on the matrix
  * cores with fp32 accumulation.  Every element of y is overwritten.  When the
  * output has few 256 x 128 tiles the K range is split across workgroups whose

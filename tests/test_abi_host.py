@@ -84,7 +84,7 @@ def test_gemm_validation(q, name, kmul):
     assert f(W, X, Y, 3, -1, kmul, None) == q.QGEMV_E_SHAPE
     assert f(W, X, Y, 3, 4, 0, None) == q.QGEMV_E_SHAPE
     assert f(W, X, Y, 3, 4, kmul + kmul // 2, None) == q.QGEMV_E_SHAPE
-    assert f(W, X, Y, 3, 4, (1 << 21) + 256, None) == q.QGEMV_E_SHAPE  # K limit of the prefill
+    assert f(W, X, Y, 3, 4, (1 << 20) + 256, None) == q.QGEMV_E_SHAPE  # K limit of the prefill
     if name == "qgemm_nvfp4":
         assert f(W, X, Y, 3, 4, 96, None) == q.QGEMV_E_SHAPE  # whole 64-weight steps
     assert f(W, X, Y, 0, 4, kmul, None) == q.QGEMV_OK  # empty: no-op, no launch

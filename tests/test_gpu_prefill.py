@@ -5,9 +5,9 @@ Bar: |y - y_ref| <= 1e-3 * sum_i |x_i w_i| + 1e-5 per output.  The weights
 enter the matrix unit rounded once to the activation type (relative error at
 most 2^-11 for fp16, 2^-8 for bf16, the latter only for NVFP4 whose weights
 are exact in bf16), which stays inside that bound; accumulation is fp32.
-Shapes cover single tokens, ragged token and row tiles (256 tokens x 128 rows
-per workgroup), odd and even K step counts, split and unsplit K and the
-Llama-8B prefill shapes (sampled outputs there).
+Shapes cover single tokens, ragged token and row tiles (256 or 512 tokens x
+128 rows per workgroup), odd and even K step counts, split and unsplit K and
+the Llama-8B prefill shapes (sampled outputs there).
 """
 import numpy as np
 import pytest
@@ -58,6 +58,11 @@ CASES = [
     ("tq1", 256, 256, 768, None, None),
     # many tiles, no K split
     ("q4k", 2048, 4096, 4096, 24, 200),
+    # enough tiles for 512-token tiles: the large prefill shape, and ragged
+    # token tiles of that kernel
+    ("q4k", 4096, 14336, 4096, 16, 200),
+    ("nvfp4", 2049, 16384, 512, 24, 300),
+    ("tq1", 1100, 32768, 512, 24, 300),
 ]
 
 
