@@ -443,9 +443,16 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
     }
 }
 
+// Clears y[0 .. count): 16 bytes per thread from the first 16-byte boundary
+// on, the head and tail floats one by one (y is only 4-byte aligned).
 __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ y, int64_t count) {
+  const int64_t head = min(count, (int64_t)((16 - (reinterpret_cast<uintptr_t>(y) & 15)) & 15) / 4);
+  const int64_t quads = (count - head) / 4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < count) y[i] = 0.f;
+  if (i < quads) reinterpret_cast<u32x4*>(y + head)[i] = u32x4{0u, 0u, 0u, 0u};
+  if (i < head) y[i] = 0.f;
+  const int64_t tail = head + 4 * quads;
+  if (i < count - tail) y[tail + i] = 0.f;
 }
 
 // Tiles of 256 or 512 tokens x 128 rows, one workgroup per CU.  When there are
@@ -474,7 +481,8 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
   split = (steps + split_steps - 1) / split_steps;
   if (split > 1) {
     const int64_t count = t * n;
-    hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, y, count);
+    const int64_t threads = count / 4 + 4;  // the 16-byte stores, and at least the 3 + 3 loose floats
+    hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y, count);
   }
   const dim3 grid((unsigned)row_tiles, (unsigned)((t + bt - 1) / bt), (unsigned)split);
   if (bt == 512)

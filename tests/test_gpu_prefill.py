@@ -85,6 +85,24 @@ def test_prefill(q, fmt, t, m, k, st, sr):
                            f"{rows[bad[0][1]]}: {g[tuple(bad[0])]} vs {yr[tuple(bad[0])]}")
 
 
+def test_prefill_split_k_unaligned_y(q):
+    # few tiles, so K is split and y is cleared first; y starts 4 bytes past
+    # a 16-byte boundary and its length is not a multiple of 4 (the clear's
+    # loose head and tail floats); the float before y must stay untouched
+    fmt, t, m, k = "q4k", 5, 299, 2304
+    w = synth.weights(fmt, m, k, synth.W_SEED + 41)
+    x = _x(fmt, t, k, synth.X_SEED + 41)
+    buf = torch.full((t * m + 8,), 7.0, dtype=torch.float32, device=DEV)
+    y = buf[1:1 + t * m].view(t, m)
+    q.GEMM[fmt](torch.from_numpy(w).to(DEV), torch.from_numpy(x.view(np.int16).copy()).to(DEV), y, t, m, k)
+    torch.cuda.synchronize()
+    yr, ar = oracle.gemm(fmt, w, x, t, m, k)
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - yr) <= 1e-3 * ar + 1e-5)
+    rest = buf.cpu().numpy()
+    assert rest[0] == 7.0 and np.all(rest[1 + t * m:] == 7.0)
+
+
 def test_prefill_empty_is_noop(q):
     w = torch.zeros(144, dtype=torch.uint8, device=DEV)
     y = torch.zeros(1, device=DEV)
