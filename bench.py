@@ -277,7 +277,8 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
 def time_graph(launch, count, steps, warmup, stream):
     """Average microseconds of one of `count` distinct launches (launch(i, h)
     enqueues number i on stream handle h), captured together in one HIP graph
-    and replayed; every copy first touched once, eagerly."""
+    and replayed; every copy first touched once, eagerly, and the timed
+    replays queued right behind the warm-up replays."""
     import torch
 
     h = stream.cuda_stream
@@ -295,7 +296,8 @@ def time_graph(launch, count, steps, warmup, stream):
             g.replay()
     reps = max(1, steps // count)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # no synchronize between the warm-up replays and the timed ones: after an
+    # idle gap the part's clocks ramp up again over the first ~0.75 ms of work
     ev0.record(stream)
     with torch.cuda.stream(stream):
         for _ in range(reps):
@@ -435,8 +437,7 @@ def measure_prefill(steps, warmup):
                 for _ in range(3):
                     torch.matmul(xf, wf.t())
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            ev0.record(stream)
+            ev0.record(stream)  # right behind the warm-up products, as in time_graph
             with torch.cuda.stream(stream):
                 for _ in range(10):
                     torch.matmul(xf, wf.t())
