@@ -110,6 +110,41 @@ def _addr(t) -> int:
     return t.data_ptr()
 
 
+# bytes of a packed weight matrix of M rows and K columns, per entry point suffix
+def weight_bytes(fmt: str, M: int, K: int) -> int:
+    if fmt == "q4k":
+        return M * (K // 256) * 144
+    if fmt == "nvfp4":
+        return M * (K // 2) + M * (K // 16)
+    if fmt == "tq1":
+        return M * (K // 256) * 54
+    return M * K * 2  # f16, bf16
+
+
+def _need(t, nbytes: int, what: str, where: str, dtype=None) -> None:
+    """Raise ValueError if tensor t holds fewer than nbytes bytes (or has the
+    wrong element type); raw integer addresses are the caller's to size."""
+    if t is None or isinstance(t, int):
+        return
+    if dtype is not None and t.dtype not in dtype:
+        raise ValueError(f"{where}: {what} must be {' or '.join(str(d) for d in dtype)}, not {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{where}: {what} holds {have} bytes, the call needs {nbytes}")
+
+
+def _f32():
+    import torch
+
+    return (torch.float32,)
+
+
+def _i16():
+    import torch
+
+    return (torch.float16, torch.bfloat16, torch.int16, torch.uint16)
+
+
 def _stream(stream) -> int:
     if stream is None:
         import torch
@@ -126,6 +161,10 @@ def _check(rc: int, where: str) -> None:
 
 
 def _gemv(name, w, x, y, M, K, stream):
+    if M > 0 and K > 0:
+        _need(w, weight_bytes(name.split("_")[1], M, K), "w", name)
+        _need(x, 2 * K, "x", name, _i16())
+        _need(y, 4 * M, "y", name, _f32())
     _check(getattr(_lib, name)(_addr(w), _addr(x), _addr(y), int(M), int(K), _stream(stream)), name)
     return y
 
@@ -166,6 +205,13 @@ def dtype_code(t) -> int:
 
 
 def _gemv_ex(name, w, x, y, M, K, alpha, beta, c, stream):
+    if M > 0 and K > 0:
+        _need(w, weight_bytes(name.split("_")[1], M, K), "w", name)
+        _need(x, 2 * K, "x", name, _i16())
+        if y is not None and not isinstance(y, int):
+            _need(y, M * y.element_size(), "y", name)
+        if beta != 0 and c is not None and not isinstance(c, int):
+            _need(c, M * c.element_size(), "c", name)
     ep = Epilogue(float(alpha), float(beta), _addr(c) if c is not None else None,
                   dtype_code(c) if c is not None else QGEMV_F32, dtype_code(y))
     _check(getattr(_lib, name)(_addr(w), _addr(x), _addr(y), int(M), int(K), ctypes.byref(ep),
@@ -200,6 +246,11 @@ def _get_rows(name, w, M, K, rows, nrows, out, stream):
 
         if rows.dtype != torch.int32:
             raise ValueError("row indices must be an int32 tensor")
+        _need(rows, 4 * nrows, "rows", name)
+    if M > 0 and K > 0:
+        _need(w, weight_bytes(name.split("_")[2], M, K), "w", name)
+    if nrows > 0 and out is not None and not isinstance(out, int):
+        _need(out, nrows * K * out.element_size(), "out", name)
     _check(getattr(_lib, name)(_addr(w), int(M), int(K), _addr(rows), int(nrows), _addr(out),
                                dtype_code(out), _stream(stream)), name)
     return out
@@ -219,14 +270,23 @@ def qget_rows_tq1(w, M, K, rows, nrows, out, stream=None):
     return _get_rows("qget_rows_tq1", w, M, K, rows, nrows, out, stream)
 
 
+def _gemm_sizes(name, w, x, y, T, M, K):
+    if T > 0 and M > 0 and K > 0:
+        _need(w, weight_bytes(name.split("_")[1], M, K), "w", name)
+        _need(x, 2 * T * K, "x", name, _i16())
+        _need(y, 4 * T * M, "y", name, _f32())
+
+
 def qgemm_q4k(w, x, y, T, M, K, stream=None):
     """Prefill: y[T][M] (fp32) = x[T][K] (fp16) . dequant_Q4_K(w)^T."""
+    _gemm_sizes("qgemm_q4k", w, x, y, T, M, K)
     _check(_lib.qgemm_q4k(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K), _stream(stream)), "qgemm_q4k")
     return y
 
 
 def qgemm_nvfp4(w, x, y, T, M, K, stream=None):
     """Prefill: y[T][M] (fp32) = x[T][K] (bf16) . dequant_NVFP4(w)^T."""
+    _gemm_sizes("qgemm_nvfp4", w, x, y, T, M, K)
     _check(_lib.qgemm_nvfp4(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K), _stream(stream)),
            "qgemm_nvfp4")
     return y
@@ -234,11 +294,15 @@ def qgemm_nvfp4(w, x, y, T, M, K, stream=None):
 
 def qgemm_tq1(w, x, y, T, M, K, stream=None):
     """Prefill: y[T][M] (fp32) = x[T][K] (fp16) . dequant_TQ1_0(w)^T."""
+    _gemm_sizes("qgemm_tq1", w, x, y, T, M, K)
     _check(_lib.qgemm_tq1(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K), _stream(stream)), "qgemm_tq1")
     return y
 
 
 def _dequant(name, w, out, M, K, stream):
+    if M > 0 and K > 0:
+        _need(w, weight_bytes(name.split("_")[1], M, K), "w", name)
+        _need(out, 4 * M * K, "out", name, _f32())
     _check(getattr(_lib, name)(_addr(w), _addr(out), int(M), int(K), _stream(stream)), name)
     return out
 

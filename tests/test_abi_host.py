@@ -167,5 +167,46 @@ def test_binding_rejects_host_tensors(q):
     import torch
 
     w = torch.zeros(144, dtype=torch.uint8)
-    with pytest.raises(ValueError):
-        q.qgemv_q4k(w, w, w, 1, 256)
+    x = torch.zeros(256, dtype=torch.float16)
+    y = torch.zeros(1, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device memory"):
+        q.qgemv_q4k(w, x, y, 1, 256)
+
+
+def test_binding_checks_tensor_sizes_and_types(q):
+    # checked before any address is taken, so host tensors reach these checks
+    import torch
+
+    f16, f32, u8 = torch.float16, torch.float32, torch.uint8
+    w, x, y = torch.zeros(2 * 144, dtype=u8), torch.zeros(256, dtype=f16), torch.zeros(2, dtype=f32)
+    with pytest.raises(ValueError, match="w holds 144 bytes"):
+        q.qgemv_q4k(w[:144], x, y, 2, 256)
+    with pytest.raises(ValueError, match="x holds"):
+        q.qgemv_q4k(w, x[:255], y, 2, 256)
+    with pytest.raises(ValueError, match="y holds"):
+        q.qgemv_q4k(w, x, y[:1], 2, 256)
+    with pytest.raises(ValueError, match="y must be"):
+        q.qgemv_q4k(w, x, torch.zeros(2, dtype=f16), 2, 256)
+    with pytest.raises(ValueError, match="x must be"):
+        q.qgemv_q4k(w, torch.zeros(256, dtype=f32), y, 2, 256)
+    with pytest.raises(ValueError, match="w holds"):
+        q.qgemv_nvfp4(torch.zeros(2 * 128 + 2 * 16 - 1, dtype=u8), x, y, 2, 256)
+    with pytest.raises(ValueError, match="w holds"):
+        q.qgemv_bf16(torch.zeros(2 * 256 * 2 - 1, dtype=u8), x, y, 2, 256)
+    # output stage: y in its own type, c only when beta != 0
+    with pytest.raises(ValueError, match="y holds"):
+        q.qgemv_q4k_ex(w, x, torch.zeros(1, dtype=f16), 2, 256)
+    with pytest.raises(ValueError, match="c holds"):
+        q.qgemv_q4k_ex(w, x, torch.zeros(2, dtype=f16), 2, 256, beta=1.0, c=torch.zeros(1, dtype=f32))
+    # prefill, rows, materialisation
+    with pytest.raises(ValueError, match="y holds"):
+        q.qgemm_q4k(w, torch.zeros(3 * 256, dtype=f16), torch.zeros(5, dtype=f32), 3, 2, 256)
+    with pytest.raises(ValueError, match="x holds"):
+        q.qgemm_tq1(torch.zeros(2 * 54, dtype=u8), torch.zeros(2 * 256, dtype=f16), torch.zeros(6, dtype=f32),
+                    3, 2, 256)
+    with pytest.raises(ValueError, match="out holds"):
+        q.qget_rows_q4k(w, 2, 256, None, 2, torch.zeros((1, 256), dtype=f16))
+    with pytest.raises(ValueError, match="rows holds"):
+        q.qget_rows_q4k(w, 2, 256, torch.zeros(1, dtype=torch.int32), 2, torch.zeros((2, 256), dtype=f16))
+    with pytest.raises(ValueError, match="out must be"):
+        q.qdequant_q4k(w, torch.zeros((2, 256), dtype=f16), 2, 256)
