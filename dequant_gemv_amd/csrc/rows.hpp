@@ -65,6 +65,24 @@ __device__ __forceinline__ uint64_t load_le_a2(__amdgpu_buffer_rsrc_t r, uint32_
   return v;
 }
 
+// The same bytes from aligned dword loads, realigned with alignbyte (off is
+// 2-byte aligned): BYTES / 4 + 1 single-dword loads instead of BYTES / 2
+// 16-bit ones.  A dword wholly or partly past the range reads as zero, so
+// the bytes past the end of the range must not be needed.
+template <int BYTES>
+__device__ __forceinline__ uint64_t load_le_a2_dw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static_assert(BYTES == 4 || BYTES == 8, "4 or 8 bytes");
+  const uint32_t al = off & ~3u, sh = off & 3u;
+  const unsigned d0 = ld32(r, al), d1 = ld32(r, al + 4u);
+  const unsigned lo = __builtin_amdgcn_alignbyte(d1, d0, sh);
+  if constexpr (BYTES == 4) {
+    return lo;
+  } else {
+    const unsigned d2 = ld32(r, al + 8u);
+    return (uint64_t)lo | ((uint64_t)__builtin_amdgcn_alignbyte(d2, d1, sh) << 32);
+  }
+}
+
 // Source row of output row j, or -1 when the index is outside [0, n).
 __device__ __forceinline__ int source_row(const int32_t* rows, int j, int n) {
   const int r = rows ? rows[j] : j;

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) void tq1_rows_kernel(const uint8_t* __restrict
         // every lane issues the same loads, with no branch around them
         const uint32_t off = e < 160 ? (e & 31) : (e >= 240 ? 48 : 32 + ((e - 160) & 15));
         Tq1RowIn in;
-        in.bytes = load_le_a2<E>(wr, blk + off);
+        in.bytes = load_le_a2_dw<E>(wr, blk + off);
         in.d = ld16(wr, blk + 52);
         return in;
       },
