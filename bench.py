@@ -401,7 +401,7 @@ PREFILL_CASES = [
 ]
 
 
-def measure_prefill(steps, warmup):
+def measure_prefill(steps, warmup, cases=None, unfused=True):
     """Prefill (many tokens): y = X . dequant(W)^T on the matrix cores, in
     TFLOP/s of 2 T N K flops; for Q4_K also the unfused path (materialise W
     as fp16 with the row kernel, then the library fp16 GEMM) for comparison."""
@@ -413,7 +413,7 @@ def measure_prefill(steps, warmup):
     dev = torch.device("cuda:0")
     out = {}
     stream = torch.cuda.Stream()
-    for fmt, t, n, k in PREFILL_CASES:
+    for fmt, t, n, k in cases or PREFILL_CASES:
         w0 = torch.from_numpy(synth.weights(fmt, n, k, 4200)).to(dev)
         ws = [w0] + [w0.clone() for _ in range(3)]
         xs = np.stack([synth.activations(fmt, k, 4300 + i) for i in range(t)])
@@ -428,7 +428,7 @@ def measure_prefill(steps, warmup):
             "tflops": round(flops / us / 1e6, 1),
             "pct_of_mfma_peak": round(100 * flops / us / 1e6 / MFMA_PEAK_TFLOPS, 1),
         }
-        if fmt == "q4k":
+        if fmt == "q4k" and unfused:
             wf = torch.empty((n, k), dtype=torch.float16, device=dev)
             us_rows = time_graph(lambda i, h: qgemv.qget_rows_q4k(ws[i], n, k, None, n, wf, h), 4,
                                  max(16, steps // 80), max(8, warmup // 80), stream)
@@ -508,6 +508,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 64 MiB device copy (a known-size reference for the HBM byte counters)")
     ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--prefill-only", default=None, metavar="FMT,T,N,K",
+                    help="time only this prefill case (e.g. q4k,4096,14336,4096) and print its record")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -524,6 +526,12 @@ def main():
     if want != have:
         print(f"libqgemv.so build id {have} does not match the sources ({want}); rebuild", file=sys.stderr)
         sys.exit(3)
+
+    if args.prefill_only:
+        f, t, n, k = args.prefill_only.split(",")
+        res = measure_prefill(args.steps, args.warmup, [(f, int(t), int(n), int(k))], unfused=False)
+        print(json.dumps({"prefill": res, "build_id": have}), flush=True)
+        return
 
     if args.calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)

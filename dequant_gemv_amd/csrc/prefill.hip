@@ -19,8 +19,9 @@
 // of 32 x 32).  Per step:
 //  - the activations of the tile (BT x 64 values, 32 or 64 KiB) go straight from
 //    global memory into LDS (buffer loads with the LDS bit, no registers);
-//    row t's 16-byte granule g sits at position g ^ (t & 7) of its 128-byte
-//    LDS row, so that the lanes of a fragment read hit different banks;
+//    row t's 16-byte granule g sits at position g ^ ((t / 2) % 8) of its
+//    128-byte LDS row, so that the lanes of a fragment read hit different
+//    banks;
 //  - each thread dequantises 16 weights of one weight row of the step (the
 //    format's functor: packed bytes straight from global memory into
 //    registers, one rounding to the MFMA input type) and writes them to LDS
@@ -48,8 +49,12 @@ constexpr int kPfWaves = 8;
 // reads zero without touching memory.
 constexpr uint32_t kPfDead = 0x80000000u;
 
-// LDS byte offset of 16-byte granule g (0..7) of tile row t.
-__device__ __forceinline__ int pf_off(int t, int g) { return t * kPfRowB + 16 * (g ^ (t & 7)); }
+// LDS byte offset of 16-byte granule g (0..7) of tile row t.  Rows are 128
+// bytes, so the 256-byte bank space of the LDS holds two: the granules of a
+// row pair are permuted by (t / 2) % 8, and any 16 consecutive rows put a
+// given granule in 16 different 16-byte bank groups (a fragment read of 16
+// rows, or the 16 lanes of a store, is conflict-free).
+__device__ __forceinline__ int pf_off(int t, int g) { return t * kPfRowB + 16 * (g ^ ((t >> 1) & 7)); }
 
 // fp16 pair (fma(a_H, s, m), fma(b_H, s, m)), each rounded once from the
 // exact value, where a_H, b_H are the fp16 values in half H of a and b:
@@ -307,15 +312,17 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
 
   // Activation copy: wave v copies tile rows 8C v .. 8C v + 8C - 1 of a step
   // in C = kPfCopies wave-wide loads of 8 rows; lane i of load j lands at LDS
-  // row 8C v + 8 j + i / 8, position i % 8, which holds granule (i % 8) ^
-  // (i / 8) of the row.
-  const uint32_t xlane =
-      (uint32_t)(8 * kPfCopies * wave + (lane >> 3)) * xrow + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  // row t = 8C v + 8 j + i / 8, position i % 8, which holds granule (i % 8) ^
+  // ((t / 2) % 8) = (i % 8) ^ (i / 16) ^ (4 if j is odd) of the row.
+  const uint32_t xrow_l = (uint32_t)(8 * kPfCopies * wave + (lane >> 3)) * xrow;
+  const uint32_t xlane0 = xrow_l + 16u * (uint32_t)((lane & 7) ^ (lane >> 4));
+  const uint32_t xlane1 = xrow_l + 16u * (uint32_t)((lane & 7) ^ (lane >> 4) ^ 4);
   auto copy_x = [&](unsigned char* stage, int s) {
     const uint32_t so = s < steps ? (uint32_t)(s_begin + s) * 128u : kPfDead;  // uniform
 #pragma unroll
     for (int j = 0; j < kPfCopies; ++j)
-      ld128_lds_s(xr, stage + (8 * kPfCopies * wave + 8 * j) * kPfRowB, xlane, so + (uint32_t)j * 8u * xrow);
+      ld128_lds_s(xr, stage + (8 * kPfCopies * wave + 8 * j) * kPfRowB, j & 1 ? xlane1 : xlane0,
+                  so + (uint32_t)j * 8u * xrow);
   };
 
   // Weight decode: thread i takes weights [16 dq, 16 dq + 16) of weight row
