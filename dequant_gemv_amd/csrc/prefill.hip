@@ -279,29 +279,30 @@ constexpr int kPfUnroll = 6;  // steps per loop iteration (a multiple of XS, 2 a
 // compile time (the loop runs kPfUnroll steps per iteration): the compiler
 // then knows that the copies in flight into one stage never alias the
 // fragment reads of another, and does not wait for them there.
-template <typename F, int BT>
-__global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t* __restrict__ w,
-                                                                  const uint16_t* __restrict__ x,
-                                                                  float* __restrict__ y, int t_count, int n,
-                                                                  int k, int split_steps) {
+// One workgroup's tile: tokens t0 .. t0 + BT - 1, weight rows n0 .. n0 + 127,
+// K split z (steps [z * split_steps, ...)), with XS activation stages in the
+// LDS arrays xs0..xs2 (at least BT * 128 bytes each, xs2 used when XS = 3)
+// and the weight stages ws0, ws1; the partial sums are added into y with
+// atomics when `atomic` (a K split), stored otherwise.
+template <typename F, int BT, int XS>
+__device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ w, const uint16_t* __restrict__ x,
+                                             float* __restrict__ y, int t_count, int n, int k, int split_steps,
+                                             int t0, int n0, int z, bool atomic, unsigned char* xs0,
+                                             unsigned char* xs1, unsigned char* xs2, unsigned char* ws0,
+                                             unsigned char* ws1) {
   static_assert(BT == 256 || BT == 512, "256 or 512 tokens per tile");
   constexpr int kPfBT = BT;                       // tokens per workgroup tile
   constexpr int kPfXTile = BT * kPfRowB;          // 32 or 64 KiB of activations per stage
-  constexpr int kPfXS = BT == 512 ? 2 : 3;        // activation stages (as many as fit the LDS)
+  constexpr int kPfXS = XS;                       // activation stages
   constexpr int kPfMI = BT / 128;                 // 32-token MFMA tiles per wave (waves are 4 x 2)
   constexpr int kPfCopies = BT / 64;              // 1 KiB activation copies per wave per step
+  static_assert(XS == 2 || XS == 3, "two or three activation stages");
   static_assert(kPfXS * kPfXTile + 2 * kPfWTile <= 160 * 1024, "activation and weight stages fit the LDS");
-  __shared__ __attribute__((aligned(1024))) unsigned char xs0[kPfXTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char xs1[kPfXTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char xs2[kPfXS == 3 ? kPfXTile : 16];
-  __shared__ __attribute__((aligned(1024))) unsigned char ws0[kPfWTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char ws1[kPfWTile];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = blockIdx.y * kPfBT, n0 = blockIdx.x * kPfBN;
-  // K split z of gridDim.z: steps [z * split_steps, ...) of the K / 64 steps
-  const int s_begin = blockIdx.z * split_steps;
+  // K split z: steps [z * split_steps, ...) of the K / 64 steps
+  const int s_begin = z * split_steps;
   const int steps = min(split_steps, k / kPfKS - s_begin);
   const uint32_t xrow = (uint32_t)k * 2u;  // bytes per activation row
 
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
         for (int j = 0; j < 2; ++j) {
           const int col = n0 + wn + 32 * j + fl;
           if (col < n) {
-            if (gridDim.z == 1)
+            if (!atomic)
               yr[col] = acc[i][j][r];
             else
               atomicAdd(yr + col, acc[i][j][r]);  // partial sum of one K split (y zeroed first)
@@ -448,6 +449,49 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t
         }
       }
     }
+}
+
+template <typename F, int BT>
+__global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t* __restrict__ w,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  float* __restrict__ y, int t_count, int n,
+                                                                  int k, int split_steps) {
+  constexpr int XS = BT == 512 ? 2 : 3;  // as many activation stages as fit the LDS
+  __shared__ __attribute__((aligned(1024))) unsigned char xs0[BT * kPfRowB];
+  __shared__ __attribute__((aligned(1024))) unsigned char xs1[BT * kPfRowB];
+  __shared__ __attribute__((aligned(1024))) unsigned char xs2[XS == 3 ? BT * kPfRowB : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char ws0[kPfWTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char ws1[kPfWTile];
+  prefill_tile<F, BT, XS>(w, x, y, t_count, n, k, split_steps, blockIdx.y * BT, blockIdx.x * kPfBN, blockIdx.z,
+                          gridDim.z > 1, xs0, xs1, xs2, ws0, ws1);
+}
+
+// 512-token tiles whose count leaves a last round at most a quarter full: the
+// first n_full tiles (whole rounds of workgroups, in index order) run over
+// all of K and store their sums; each remaining tile is split over K into
+// tail_split parts of split_steps steps whose workgroups fill the last round
+// together and add their partial sums into y with atomics (the rows of those
+// tiles are zeroed first).
+template <typename F>
+__global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_tail_kernel(const uint8_t* __restrict__ w,
+                                                                       const uint16_t* __restrict__ x,
+                                                                       float* __restrict__ y, int t_count, int n,
+                                                                       int k, int row_tiles, int n_full,
+                                                                       int tail_split, int split_steps) {
+  __shared__ __attribute__((aligned(1024))) unsigned char xs0[512 * kPfRowB];
+  __shared__ __attribute__((aligned(1024))) unsigned char xs1[512 * kPfRowB];
+  __shared__ __attribute__((aligned(1024))) unsigned char xs2[16];
+  __shared__ __attribute__((aligned(1024))) unsigned char ws0[kPfWTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char ws1[kPfWTile];
+  const int b = blockIdx.x;
+  int tile = b, z = 0, ss = k / kPfKS;
+  if (b >= n_full) {
+    tile = n_full + (b - n_full) / tail_split;
+    z = (b - n_full) % tail_split;
+    ss = split_steps;
+  }
+  prefill_tile<F, 512, 2>(w, x, y, t_count, n, k, ss, (tile / row_tiles) * 512, (tile % row_tiles) * kPfBN, z,
+                          b >= n_full, xs0, xs1, xs2, ws0, ws1);
 }
 
 // Clears y[0 .. count): 16 bytes per thread from the first 16-byte boundary
@@ -467,7 +511,8 @@ __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ y
 // least 8 steps per split) and the splits add their partial sums into y with
 // fp32 atomics, y being cleared by a fill kernel first (a kernel, so that the
 // sequence can be captured in a graph); the order of those few additions
-// varies from run to run.
+// varies from run to run.  When 512-token tiles leave a last round at most
+// a quarter full, only the tiles of that round are split (prefill_tail_kernel).
 template <typename F>
 static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
                                  hipStream_t s) {
@@ -490,6 +535,29 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
     const int64_t count = t * n;
     const int64_t threads = count / 4 + 4;  // the 16-byte stores, and at least the 3 + 3 loose floats
     hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y, count);
+  }
+  if (bt == 512 && split == 1 && tiles % 256 != 0 && tiles % 256 <= 64) {
+    // the last round would be at most a quarter full: split its tiles over K
+    // so that it takes about 1 / tail_split of a round.  (A half-full last
+    // round is left alone: splitting it measured 2 % slower at 4096 tokens x
+    // 14336 rows, the clock of the power-limited chip being higher while
+    // half of it idles, and the clear and atomics costing extra.)
+    const int64_t tail = tiles % 256, n_full = tiles - tail;
+    int64_t tail_split = min(256 / tail, int64_t(4));
+    tail_split = min(tail_split, max(int64_t(1), steps / 12));
+    const int64_t tail_steps = ((steps + tail_split - 1) / tail_split + kPfUnroll - 1) / kPfUnroll * kPfUnroll;
+    tail_split = (steps + tail_steps - 1) / tail_steps;
+    if (tail_split > 1) {
+      const int64_t t_zero = n_full / row_tiles * 512;  // first token row of a split tile
+      const int64_t count = (t - t_zero) * n;
+      const int64_t threads = count / 4 + 4;
+      hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                         y + t_zero * n, count);
+      hipLaunchKernelGGL((prefill_tail_kernel<F>), dim3((unsigned)(n_full + tail * tail_split)),
+                         dim3(64 * kPfWaves), 0, s, (const uint8_t*)w, (const uint16_t*)x, y, (int)t, (int)n,
+                         (int)k, (int)row_tiles, (int)n_full, (int)tail_split, (int)tail_steps);
+      return hipGetLastError();
+    }
   }
   const dim3 grid((unsigned)row_tiles, (unsigned)((t + bt - 1) / bt), (unsigned)split);
   if (bt == 512)

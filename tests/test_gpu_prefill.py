@@ -85,6 +85,31 @@ def test_prefill(q, fmt, t, m, k, st, sr):
                            f"{rows[bad[0][1]]}: {g[tuple(bad[0])]} vs {yr[tuple(bad[0])]}")
 
 
+@pytest.mark.parametrize("fmt,t,m,k", [("q4k", 1025, 21888, 4096), ("tq1", 1025, 21888, 2048)])
+def test_prefill_tail_round_split(q, fmt, t, m, k):
+    # 171 row tiles x 3 token tiles of 512 = 513 tiles: two full rounds on
+    # 256 CUs and one tile left, which is split over K (4 parts of 18, 18,
+    # 18 and 10 steps for K = 4096, 2 parts of 18 and 14 steps for K = 2048)
+    # into token 1024 x rows 21760.. 21887; the other tiles of that token row
+    # are stored unsplit over a cleared y
+    seed = 900 + k % 89
+    w = synth.weights(fmt, m, k, synth.W_SEED + seed)
+    x = _x(fmt, t, k, synth.X_SEED + seed)
+    y = torch.full((t, m), float("nan"), dtype=torch.float32, device=DEV)
+    q.GEMM[fmt](torch.from_numpy(w).to(DEV), torch.from_numpy(x.view(np.int16).copy()).to(DEV), y, t, m, k)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([[0, 511, 512, 1023, 1024], rng.integers(0, t, 12)]))
+    rows = np.unique(np.concatenate([np.arange(21760, m, 3), [0, 127, 21759], rng.integers(0, m, 60)]))
+    yr, ar = oracle.gemm(fmt, w, x, t, m, k, tokens=toks, rows=rows)
+    g = got[np.ix_(toks, rows)]
+    bad = np.argwhere(~(np.abs(g - yr) <= 1e-3 * ar + 1e-5))
+    assert bad.size == 0, (f"{fmt} T={t} {m}x{k}: {len(bad)} outputs off, e.g. token {toks[bad[0][0]]} row "
+                           f"{rows[bad[0][1]]}: {g[tuple(bad[0])]} vs {yr[tuple(bad[0])]}")
+    assert not np.isnan(got).any()
+
+
 def test_prefill_split_k_unaligned_y(q):
     # few tiles, so K is split and y is cleared first; y starts 4 bytes past
     # a 16-byte boundary and its length is not a multiple of 4 (the clear's
