@@ -536,7 +536,9 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
     const int64_t threads = count / 4 + 4;  // the 16-byte stores, and at least the 3 + 3 loose floats
     hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y, count);
   }
-  if (bt == 512 && split == 1 && tiles % 256 != 0 && tiles % 256 <= 64) {
+  // (the one-dimensional grid and the clear stay well inside 32-bit counts)
+  if (bt == 512 && split == 1 && tiles % 256 != 0 && tiles % 256 <= 64 && tiles < (int64_t(1) << 28) &&
+      n < (int64_t(1) << 24)) {
     // the last round would be at most a quarter full: split its tiles over K
     // so that it takes about 1 / tail_split of a round.  (A half-full last
     // round is left alone: splitting it measured 2 % slower at 4096 tokens x

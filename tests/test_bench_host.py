@@ -1,0 +1,53 @@
+"""Host-side logic of bench.py: the one-GPU guard, the algorithmic byte count
+behind the metric and the reading of the committed HBM-byte summary (no GPU)."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _golden():
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "roofline_bytes.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            key, val = line.split()
+            vals[key] = int(val)
+    return vals
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_metric_bytes_match_the_roofline_section():
+    # weights (144 B per 256 weights) + fp16 x + fp32 y of the metric's shape
+    g = _golden()
+    fmt, n, k, _ = bench.MAIN
+    assert (fmt, n, k) == ("q4k", 4096, 14336)
+    want = g["q4k_weight_bytes_4096x14336"] + g["q4k_x_bytes_14336"] + g["q4k_y_bytes_4096"]
+    assert bench.algorithmic_bytes(fmt, n, k) == want == 33075200
+
+
+def test_traffic_only_from_a_summary_of_the_same_build(tmp_path, monkeypatch):
+    p = tmp_path / "summary.md"
+    p.write_text("# HBM bytes\n\ntraffic_bytes_per_launch: 33417529\ntraffic_build_id: abc123\n")
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(p))
+    assert bench.measured_traffic("abc123") == 33417529
+    assert bench.measured_traffic("def456") is None
+    p.write_text("traffic_build_id: abc123\n")
+    assert bench.measured_traffic("abc123") is None
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "missing.md"))
+    assert bench.measured_traffic("abc123") is None
+
+
+def test_committed_summary_is_parseable():
+    fields = dict(line.split(":", 1) for line in open(bench.TRAFFIC_SUMMARY) if ":" in line)
+    bid = fields["traffic_build_id"].strip()
+    assert bench.measured_traffic(bid) == int(fields["traffic_bytes_per_launch"])
