@@ -516,11 +516,17 @@ __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ y
 template <typename F>
 static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
                                  hipStream_t s) {
-  // 512-token tiles when they still fill at least two rounds of workgroups
-  // (each weight is then decoded half as often and each fragment read feeds
-  // more MFMAs), else 256-token tiles
+  // 512-token tiles decode each weight half as often and feed more MFMAs per
+  // fragment read, but one takes about 1.7 times as long as a 256-token tile
+  // (measured): they are used when they fill at least two rounds of
+  // workgroups, or when 256-token tiles need more than one round and the
+  // 512-token rounds take fewer tile-times (1024 tokens x 14336 rows: one
+  // round of 224 tiles, against two rounds of 448)
   const int64_t row_tiles = (n + kPfBN - 1) / kPfBN;
-  const int bt = row_tiles * ((t + 511) / 512) >= 512 ? 512 : 256;
+  const int64_t tiles512 = row_tiles * ((t + 511) / 512), tiles256 = row_tiles * ((t + 255) / 256);
+  const bool use512 =
+      tiles512 >= 512 || (tiles256 > 256 && 17 * ((tiles512 + 255) / 256) < 10 * ((tiles256 + 255) / 256));
+  const int bt = use512 ? 512 : 256;
   const int64_t tiles = row_tiles * ((t + bt - 1) / bt);
   const int64_t steps = k / kPfKS;
   int64_t split = 1;

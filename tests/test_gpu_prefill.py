@@ -63,6 +63,10 @@ CASES = [
     ("q4k", 4096, 14336, 4096, 16, 200),
     ("nvfp4", 2049, 16384, 512, 24, 300),
     ("tq1", 1100, 32768, 512, 24, 300),
+    # one round of 512-token tiles instead of two of 256 (ragged last tile)
+    ("nvfp4", 1000, 14336, 1024, 24, 300),
+    ("tq1", 1000, 14336, 768, 24, 300),
+    ("q4k", 2560, 4096, 2048, 24, 300),
 ]
 
 
