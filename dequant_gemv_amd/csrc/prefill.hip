@@ -494,16 +494,23 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_tail_kernel(const ui
                           b >= n_full, xs0, xs1, xs2, ws0, ws1);
 }
 
-// Clears y[0 .. count): 16 bytes per thread from the first 16-byte boundary
-// on, the head and tail floats one by one (y is only 4-byte aligned).
+// Clears y[0 .. count): 16-byte stores from the first 16-byte boundary on,
+// 1024 of them per workgroup (thread i stores the i-th of every 256, so each
+// wave-wide store is contiguous), and the at most 3 + 3 loose floats before
+// and after them one by one in workgroup 0 (y is only 4-byte aligned).
+// Launched with count / 4096 + 1 workgroups of 256 threads.
 __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ y, int64_t count) {
   const int64_t head = min(count, (int64_t)((16 - (reinterpret_cast<uintptr_t>(y) & 15)) & 15) / 4);
   const int64_t quads = (count - head) / 4;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < quads) reinterpret_cast<u32x4*>(y + head)[i] = u32x4{0u, 0u, 0u, 0u};
-  if (i < head) y[i] = 0.f;
-  const int64_t tail = head + 4 * quads;
-  if (i < count - tail) y[tail + i] = 0.f;
+  const int64_t q0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (q0 + 256 * j < quads) reinterpret_cast<u32x4*>(y + head)[q0 + 256 * j] = u32x4{0u, 0u, 0u, 0u};
+  if (blockIdx.x == 0) {
+    const int64_t tail = head + 4 * quads;
+    if (threadIdx.x < head) y[threadIdx.x] = 0.f;
+    if (threadIdx.x < count - tail) y[tail + threadIdx.x] = 0.f;
+  }
 }
 
 // Tiles of 256 or 512 tokens x 128 rows, one workgroup per CU.  When there are
@@ -539,8 +546,7 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
   split = (steps + split_steps - 1) / split_steps;
   if (split > 1) {
     const int64_t count = t * n;
-    const int64_t threads = count / 4 + 4;  // the 16-byte stores, and at least the 3 + 3 loose floats
-    hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y, count);
+    hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)(count / 4096 + 1)), dim3(256), 0, s, y, count);
   }
   // (the one-dimensional grid and the clear stay well inside 32-bit counts)
   if (bt == 512 && split == 1 && tiles % 256 != 0 && tiles % 256 <= 64 && tiles < (int64_t(1) << 28) &&
@@ -558,9 +564,8 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
     if (tail_split > 1) {
       const int64_t t_zero = n_full / row_tiles * 512;  // first token row of a split tile
       const int64_t count = (t - t_zero) * n;
-      const int64_t threads = count / 4 + 4;
-      hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                         y + t_zero * n, count);
+      hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)(count / 4096 + 1)), dim3(256), 0, s, y + t_zero * n,
+                         count);
       hipLaunchKernelGGL((prefill_tail_kernel<F>), dim3((unsigned)(n_full + tail * tail_split)),
                          dim3(64 * kPfWaves), 0, s, (const uint8_t*)w, (const uint16_t*)x, y, (int)t, (int)n,
                          (int)k, (int)row_tiles, (int)n_full, (int)tail_split, (int)tail_steps);
