@@ -274,11 +274,15 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
     return res
 
 
-def time_graph(launch, count, steps, warmup, stream):
+def time_graph(launch, count, steps, warmup, stream, min_warm_ms=0.0, min_timed_ms=0.0):
     """Average microseconds of one of `count` distinct launches (launch(i, h)
     enqueues number i on stream handle h), captured together in one HIP graph
     and replayed; every copy first touched once, eagerly, and the timed
-    replays queued right behind the warm-up replays."""
+    replays queued right behind the warm-up replays.  With min_warm_ms /
+    min_timed_ms the warm-up and the timed region also last at least that
+    long (long kernels: the clocks take several ms of load to settle)."""
+    import math
+
     import torch
 
     h = stream.cuda_stream
@@ -291,10 +295,20 @@ def time_graph(launch, count, steps, warmup, stream):
         for i in range(count):
             launch(i, h)
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, warmup // count)):
+    warm_reps, reps = max(1, warmup // count), max(1, steps // count)
+    if min_warm_ms > 0 or min_timed_ms > 0:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        with torch.cuda.stream(stream):
             g.replay()
-    reps = max(1, steps // count)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per = max(e0.elapsed_time(e1), 1e-3)  # ms per replay
+        warm_reps = max(warm_reps, math.ceil(min_warm_ms / per))
+        reps = max(reps, math.ceil(min_timed_ms / per))
+    with torch.cuda.stream(stream):
+        for _ in range(warm_reps):
+            g.replay()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # no synchronize between the warm-up replays and the timed ones: after an
     # idle gap the part's clocks ramp up again over the first ~0.75 ms of work
@@ -396,15 +410,24 @@ MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of the part
 PREFILL_CASES = [
     # (format, tokens, weight rows, K)
     ("q4k", 512, 4096, 14336), ("q4k", 512, 14336, 4096), ("q4k", 4096, 14336, 4096),
+    ("q4k", 4096, 4096, 14336), ("q4k", 1024, 14336, 4096),
     ("nvfp4", 512, 4096, 14336), ("nvfp4", 512, 14336, 4096),
     ("tq1", 512, 4096, 14336), ("tq1", 512, 14336, 4096),
 ]
+
+
+# prefill launches run 0.1-0.6 ms: warm up and time each case for at least
+# this long, so that every case is timed at settled clocks
+PREFILL_WARM_MS = 25.0
+PREFILL_TIMED_MS = 15.0
 
 
 def measure_prefill(steps, warmup, cases=None, unfused=True):
     """Prefill (many tokens): y = X . dequant(W)^T on the matrix cores, in
     TFLOP/s of 2 T N K flops; for Q4_K also the unfused path (materialise W
     as fp16 with the row kernel, then the library fp16 GEMM) for comparison."""
+    import math
+
     import numpy as np
     import torch
 
@@ -420,7 +443,8 @@ def measure_prefill(steps, warmup, cases=None, unfused=True):
         x = torch.from_numpy(xs.view(np.int16)).to(dev)
         y = torch.empty((t, n), dtype=torch.float32, device=dev)
         fn = qgemv.GEMM[fmt]
-        us = time_graph(lambda i, h: fn(ws[i], x, y, t, n, k, h), 4, max(16, steps // 80), max(8, warmup // 80), stream)
+        us = time_graph(lambda i, h: fn(ws[i], x, y, t, n, k, h), 4, max(16, steps // 80), max(8, warmup // 80), stream,
+                        PREFILL_WARM_MS, PREFILL_TIMED_MS)
         flops = 2.0 * t * n * k
         rec = {
             "workload": f"{fmt} prefill, {t} tokens x {n} rows x K {k}",
@@ -431,19 +455,27 @@ def measure_prefill(steps, warmup, cases=None, unfused=True):
         if fmt == "q4k" and unfused:
             wf = torch.empty((n, k), dtype=torch.float16, device=dev)
             us_rows = time_graph(lambda i, h: qgemv.qget_rows_q4k(ws[i], n, k, None, n, wf, h), 4,
-                                 max(16, steps // 80), max(8, warmup // 80), stream)
+                                 max(16, steps // 80), max(8, warmup // 80), stream, PREFILL_WARM_MS,
+                                 PREFILL_TIMED_MS)
             xf = x.view(torch.float16)
-            with torch.cuda.stream(stream):
-                for _ in range(3):
-                    torch.matmul(xf, wf.t())
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            with torch.cuda.stream(stream):
+                torch.matmul(xf, wf.t())
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            per = max(ev0.elapsed_time(ev1), 1e-3)  # ms, a first estimate
+            n_mm = max(10, math.ceil(PREFILL_TIMED_MS / per))
+            with torch.cuda.stream(stream):
+                for _ in range(max(3, math.ceil(PREFILL_WARM_MS / per))):
+                    torch.matmul(xf, wf.t())
             ev0.record(stream)  # right behind the warm-up products, as in time_graph
             with torch.cuda.stream(stream):
-                for _ in range(10):
+                for _ in range(n_mm):
                     torch.matmul(xf, wf.t())
             ev1.record(stream)
             torch.cuda.synchronize()
-            us_mm = 1e3 * ev0.elapsed_time(ev1) / 10
+            us_mm = 1e3 * ev0.elapsed_time(ev1) / n_mm
             rec["unfused_us"] = round(us_rows + us_mm, 2)
             rec["unfused_note"] = (f"fp16 materialisation {us_rows:.1f} us + library fp16 GEMM {us_mm:.1f} us "
                                    f"({flops / us_mm / 1e6:.0f} TFLOP/s)")
