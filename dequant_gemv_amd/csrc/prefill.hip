@@ -379,10 +379,10 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ w, cons
   wait_vm<(kPfXS == 3 ? kPfCopies : 0) + 2 * F::kLoads>();
   lds_barrier();
 
-  // Every iteration runs kPfUnroll steps with no branch between them (a
-  // branch per step makes the compiler's load-wait bookkeeping merge paths
-  // and wait for every load in flight).  Steps past `steps` load nothing, so
-  // their tiles are zero and their products add nothing.
+  // Every iteration runs kPfUnroll steps with no branch around their loads
+  // (a branch around a step's loads makes the compiler's load-wait
+  // bookkeeping merge paths and wait for every load in flight).  Steps past
+  // `steps` load nothing and skip their arithmetic.
   for (int s0 = 0; s0 < steps; s0 += kPfUnroll) {
     static_for<0, kPfUnroll>([&](auto ic) {
       constexpr int I = decltype(ic)::value;  // = s % kPfUnroll
@@ -398,6 +398,10 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ w, cons
       // (no decode arithmetic above the loads: it would wait for step s + 1's
       // weights before this step's loads are even issued)
       __builtin_amdgcn_sched_barrier(0);
+      // A step past the end (the last iteration's) skips its decode, MFMAs
+      // and weight store; the branch holds no global load, so the load waits
+      // stay exact.
+      if (s < steps) {
       unsigned v[8];
       F::make(wq[(I + 1) % kPfWQ], s_begin + s + 1, dq, v);
 #pragma unroll
@@ -423,6 +427,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ w, cons
           }
       }
       store_w(wb, v);
+      }
       wait_vm<(kPfXS - 2) * kStepLoads + F::kLoads>();  // this wave's copy of step s + 1's activations
       lds_barrier();  // all reads of this step's stages and all writes of the next are done
     });
@@ -540,8 +545,9 @@ static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t
   if (tiles < 256) split = max(int64_t(1), 256 / tiles);  // fewer tiles than CUs
   split = min(split, max(int64_t(1), steps / 8));
   split = min(split, int64_t(16));
-  // a whole number of loop iterations per split (only the last split can end
-  // in zero steps)
+  // a whole number of loop iterations per split (only the last split ends
+  // early): a step past the end skips its arithmetic but still waits for the
+  // loads in flight, and measured nearly as slow as a full one
   const int64_t split_steps = ((steps + split - 1) / split + kPfUnroll - 1) / kPfUnroll * kPfUnroll;
   split = (steps + split_steps - 1) / split_steps;
   if (split > 1) {
