@@ -26,6 +26,8 @@
  *           aborts.  M == 0 is a successful no-op.
  *   Alignment  W, x and materialised rows must be 16-byte aligned; y and c
  *              to their element size.
+ *   Limits     M <= 2^31 - 1 and K <= 2^24 (the dense GEMV: K <= 65536; the
+ *              prefill calls: K <= 2^20); larger sizes return QGEMV_E_SHAPE.
  *   Threads    calls are thread-safe (no global mutable state).
  */
 #ifndef QGEMV_H

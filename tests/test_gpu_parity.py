@@ -181,6 +181,12 @@ def test_gemv_full_shapes(q, fmt, n, k, case):
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "nvfp4", "tq1"])
+def test_gemv_max_k(q, fmt):
+    # the largest K the calls accept (2^24: 16.8 M weights per row, a 32 MB x)
+    _check_gemv(q, fmt, 3, 1 << 24, seed=90)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "nvfp4", "tq1"])
 def test_gemv_lm_head_sampled(q, fmt):
     # 128256 x 4096: 2,048 sampled rows plus the first and last
     _check_gemv(q, fmt, 128256, 4096, seed=4, sample=2048)

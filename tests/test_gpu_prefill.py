@@ -114,6 +114,22 @@ def test_prefill_tail_round_split(q, fmt, t, m, k):
     assert not np.isnan(got).any()
 
 
+@pytest.mark.parametrize("fmt", ["q4k", "nvfp4", "tq1"])
+def test_prefill_max_k(q, fmt):
+    # the largest K the prefill calls accept (2^20): two row tiles, K split
+    # 16 ways, 1024 steps per split; sampled rows of both tiles
+    t, m, k = 3, 130, 1 << 20
+    w = synth.weights(fmt, m, k, synth.W_SEED + 93)
+    x = _x(fmt, t, k, synth.X_SEED + 93)
+    y = torch.full((t, m), float("nan"), dtype=torch.float32, device=DEV)
+    q.GEMM[fmt](torch.from_numpy(w).to(DEV), torch.from_numpy(x.view(np.int16).copy()).to(DEV), y, t, m, k)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 127, 128, 129])
+    yr, ar = oracle.gemm(fmt, w, x, t, m, k, rows=rows)
+    got = y.cpu().numpy().astype(np.float64)[:, rows]
+    assert np.all(np.abs(got - yr) <= 1e-3 * ar + 1e-5), np.max(np.abs(got - yr) / (1e-3 * ar + 1e-5))
+
+
 def test_prefill_split_k_unaligned_y(q):
     # few tiles, so K is split and y is cleared first; y starts 4 bytes past
     # a 16-byte boundary and its length is not a multiple of 4 (the clear's
