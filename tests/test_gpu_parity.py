@@ -186,6 +186,27 @@ def test_gemv_max_k(q, fmt):
     _check_gemv(q, fmt, 3, 1 << 24, seed=90)
 
 
+@pytest.mark.parametrize("fmt,k", [("q4k", 256), ("nvfp4", 64), ("tq1", 256)])
+def test_gemv_twenty_million_rows(q, fmt, k):
+    # M = 20,000,003 (grids past 2^24 rows, a ragged last workgroup): the rows
+    # repeat a random block of 4099 rows (a period that no power-of-two index
+    # mistake preserves); 3000 sampled rows plus the first and last
+    n, period = 20_000_003, 4099
+    base = synth.weights(fmt, period, k, synth.W_SEED + 95)
+    if fmt == "nvfp4":  # nibbles [M][K/2], then scales [M][K/16]
+        nib, sc = base[:period * k // 2].reshape(period, k // 2), base[period * k // 2:].reshape(period, k // 16)
+        reps = (n + period - 1) // period
+        w = np.concatenate([np.tile(nib, (reps, 1))[:n].ravel(), np.tile(sc, (reps, 1))[:n].ravel()])
+    else:
+        w = np.tile(base.reshape(period, -1), ((n + period - 1) // period, 1))[:n].ravel()
+    x = synth.activations(fmt, k, synth.X_SEED + 95)
+    y = _run_gemv(q, fmt, w, x, n, k)
+    rng = np.random.default_rng(95)
+    rows = np.unique(np.concatenate([[0, 1, (1 << 24) - 1, 1 << 24, n - 2, n - 1], rng.integers(0, n, 3000)]))
+    yr, ar = oracle.gemv(fmt, w, x, n, k, rows=rows)
+    _assert_close(fmt, n, k, y[rows], yr, ar, rows)
+
+
 @pytest.mark.parametrize("fmt", ["q4k", "nvfp4", "tq1"])
 def test_gemv_lm_head_sampled(q, fmt):
     # 128256 x 4096: 2,048 sampled rows plus the first and last
