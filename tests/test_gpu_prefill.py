@@ -130,6 +130,29 @@ def test_prefill_max_k(q, fmt):
     assert np.all(np.abs(got - yr) <= 1e-3 * ar + 1e-5), np.max(np.abs(got - yr) / (1e-3 * ar + 1e-5))
 
 
+@pytest.mark.parametrize("fmt,k", [("q4k", 256), ("nvfp4", 64), ("tq1", 256)])
+def test_prefill_million_rows(q, fmt, k):
+    # M = 1,000,003 (7,813 row tiles, the last one ragged) for 3 tokens; the
+    # rows repeat a random block of 4099 rows; 2000 sampled rows
+    t, m, period = 3, 1_000_003, 4099
+    base = synth.weights(fmt, period, k, synth.W_SEED + 97)
+    reps = (m + period - 1) // period
+    if fmt == "nvfp4":  # nibbles [M][K/2], then scales [M][K/16]
+        nib, sc = base[:period * k // 2].reshape(period, k // 2), base[period * k // 2:].reshape(period, k // 16)
+        w = np.concatenate([np.tile(nib, (reps, 1))[:m].ravel(), np.tile(sc, (reps, 1))[:m].ravel()])
+    else:
+        w = np.tile(base.reshape(period, -1), (reps, 1))[:m].ravel()
+    x = _x(fmt, t, k, synth.X_SEED + 97)
+    y = torch.full((t, m), float("nan"), dtype=torch.float32, device=DEV)
+    q.GEMM[fmt](torch.from_numpy(w).to(DEV), torch.from_numpy(x.view(np.int16).copy()).to(DEV), y, t, m, k)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(97)
+    rows = np.unique(np.concatenate([[0, 127, 128, m - 3, m - 1], rng.integers(0, m, 2000)]))
+    yr, ar = oracle.gemm(fmt, w, x, t, m, k, rows=rows)
+    got = y.cpu().numpy().astype(np.float64)[:, rows]
+    assert np.all(np.abs(got - yr) <= 1e-3 * ar + 1e-5)
+
+
 def test_prefill_split_k_unaligned_y(q):
     # few tiles, so K is split and y is cleared first; y starts 4 bytes past
     # a 16-byte boundary and its length is not a multiple of 4 (the clear's
