@@ -348,7 +348,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
 // picks each half's 2 output bytes out of the 6-byte table (-d, 0d, +d).
 
 #ifndef QGEMV_TQ1_ROWS_U
-#define QGEMV_TQ1_ROWS_U 2  // row-materialisation tasks per thread
+#define QGEMV_TQ1_ROWS_U 8  // row-materialisation tasks per thread
 #endif
 
 struct Tq1RowIn {
