@@ -366,20 +366,23 @@ __global__ __launch_bounds__(256) void q4k_rows_kernel(const uint8_t* __restrict
   constexpr int E = kRowsE<T>;
   const int j = blockIdx.x / bpr;
   const int r = source_row(rows, j, n);
-  const uint8_t* const wr = w + (int64_t)(r < 0 ? 0 : r) * nb * kQ4kBytes;
+  // the source row as a buffer (32-bit offsets into it)
+  const auto wr = make_rsrc(w + (int64_t)(r < 0 ? 0 : r) * nb * kQ4kBytes, (uint32_t)nb * kQ4kBytes);
   T* const orow = out + (int64_t)j * nb * 256;
   rows_thread<U, Q4kRowIn>(
       bpr, nb * (256 / E), r >= 0,
       [&](int t) {
         const int e0 = t * E, e = e0 & 255;
-        const uint8_t* const blk = wr + (e0 >> 8) * kQ4kBytes;
+        const uint32_t blk = (uint32_t)(e0 >> 8) * kQ4kBytes;
         Q4kRowIn in;
-        in.hdr = *reinterpret_cast<const u32x4*>(blk);
-        const uint8_t* const qp = blk + 16 + 32 * (e >> 6) + (e & 31);
-        if constexpr (E == 8)
-          in.q = *reinterpret_cast<const uint64_t*>(qp);
-        else
-          in.q = *reinterpret_cast<const uint32_t*>(qp);
+        in.hdr = ld128s(wr, blk, 0u);
+        const uint32_t qo = blk + 16u + (uint32_t)(32 * (e >> 6) + (e & 31));
+        if constexpr (E == 8) {
+          const u32x2 q = ld64s(wr, qo, 0u);
+          in.q = (uint64_t)q.x | ((uint64_t)q.y << 32);
+        } else {
+          in.q = ld32s(wr, qo, 0u);
+        }
         return in;
       },
       [&](int t, const Q4kRowIn& in) {
@@ -391,10 +394,14 @@ __global__ __launch_bounds__(256) void q4k_rows_kernel(const uint8_t* __restrict
         const unsigned mg = (sel.mins(in.hdr.z, in.hdr.w) >> sh) & 0xFFu;
         const float ds = f16lo(in.hdr.x) * (float)sg, dm = f16hi(in.hdr.x) * (float)mg;
         const unsigned nsh = 4u * (unsigned)hi;
+        // the E nibbles as bytes 0..3 of one or two words (byte i -> weight i)
+        unsigned m[2] = {((unsigned)in.q >> nsh) & 0x0F0F0F0Fu, ((unsigned)(in.q >> 32) >> nsh) & 0x0F0F0F0Fu};
+        // opaque to the compiler, so that each byte converts with one
+        // v_cvt_f32_ubyteN (with the masked bits known it shifts first)
+        __asm__("" : "+v"(m[0]), "+v"(m[1]));
         float v[E];
 #pragma unroll
-        for (int i = 0; i < E; ++i)
-          v[i] = __builtin_fmaf(ds, (float)((unsigned)(in.q >> (8 * i + nsh)) & 15u), -dm);
+        for (int i = 0; i < E; ++i) v[i] = __builtin_fmaf(ds, (float)((m[i >> 2] >> (8 * (i & 3))) & 0xFFu), -dm);
         store_e(orow + t * E, v);
       },
       [&](int t) { store_e_nan(orow + t * E); });

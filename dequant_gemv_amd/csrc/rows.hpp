@@ -21,8 +21,13 @@ namespace qgemv {
 template <typename T>
 __device__ __forceinline__ unsigned pack2(float a, float b) {
   if constexpr (sizeof(T) == 2) {
-    const T lo = (T)pin_f32(a), hi = (T)pin_f32(b);  // fp32 value, then round to nearest even
-    return (unsigned)__builtin_bit_cast(unsigned short, lo) | ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16);
+    // fp32 values, then both rounded to nearest even by one packed conversion
+    // (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32); pinned, so that no multiply or
+    // fma before them is fused into a single-rounding mixed-precision op
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef T t2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {pin_f32(a), pin_f32(b)};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, t2_t));
   } else {
     return 0u;  // unused
   }
