@@ -542,6 +542,8 @@ def main():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--prefill-only", default=None, metavar="FMT,T,N,K",
                     help="time only this prefill case (e.g. q4k,4096,14336,4096) and print its record")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="time only the row-materialisation cases (after --calibrate-copy if given) and print them")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -573,6 +575,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("[bench] calibration: 8 copies of 64 MiB (read 65536 KiB + write 65536 KiB each)")
+
+    if args.rows_only:
+        print(json.dumps({"get_rows": measure_rows(args.steps, args.warmup, args.rotate), "build_id": have}),
+              flush=True)
+        return
 
     fmt, n, k, desc = MAIN
     if args.fmt:
