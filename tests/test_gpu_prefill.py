@@ -89,7 +89,8 @@ def test_prefill(q, fmt, t, m, k, st, sr):
                            f"{rows[bad[0][1]]}: {g[tuple(bad[0])]} vs {yr[tuple(bad[0])]}")
 
 
-@pytest.mark.parametrize("fmt,t,m,k", [("q4k", 1025, 21888, 4096), ("tq1", 1025, 21888, 2048)])
+@pytest.mark.parametrize("fmt,t,m,k", [("q4k", 1025, 21888, 4096), ("tq1", 1025, 21888, 2048),
+                                       ("nvfp4", 1025, 21888, 2048)])
 def test_prefill_tail_round_split(q, fmt, t, m, k):
     # 171 row tiles x 3 token tiles of 512 = 513 tiles: two full rounds on
     # 256 CUs and one tile left, which is split over K (4 parts of 18, 18,
