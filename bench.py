@@ -492,6 +492,34 @@ def measure_prefill(steps, warmup, cases=None, unfused=True):
     return out
 
 
+def measure_ceiling_sweep():
+    """Per-launch time of the pure-read kernel against the bytes it reads (a
+    graph of 32 launches over 32 buffers, as for the metric), and the least-
+    squares fit t = fixed + bytes / bandwidth over the launches of >= 4 MB:
+    the fixed part is what one launch costs beyond streaming its bytes."""
+    import numpy as np
+    import torch
+
+    from dequant_gemv_amd import qgemv
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    points = []
+    for mb in (0.0625, 0.25, 1, 4, 8, 16, 33.0752, 64, 128):
+        nbytes = int(mb * 1e6) // 16 * 16
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(32)]
+        sink = torch.zeros(qgemv.qgemv_read_sink_len(nbytes), dtype=torch.float32, device=dev)
+        us = time_graph(lambda i, h: qgemv.qgemv_read_ceiling(bufs[i], nbytes, sink, h), 32, 3200, 1280, stream)
+        points.append({"bytes": nbytes, "us": round(us, 3), "gbps": round(nbytes / us / 1e3, 1)})
+        log(f"[bench] read {nbytes / 1e6:.3f} MB: {us:.3f} us/launch, {nbytes / us / 1e3:.1f} GB/s")
+        del bufs, sink
+        torch.cuda.empty_cache()
+    b = np.array([p["bytes"] for p in points if p["bytes"] >= 4e6], dtype=np.float64)
+    t = np.array([p["us"] for p in points if p["bytes"] >= 4e6], dtype=np.float64)
+    (fixed, per_byte), *_ = np.linalg.lstsq(np.vstack([np.ones_like(b), b]).T, t, rcond=None)
+    return {"points": points, "fit_fixed_us": round(float(fixed), 3), "fit_gbps": round(1e-3 / float(per_byte), 1)}
+
+
 def cpu_baseline(fmt, n, k, budget_s=10.0):
     """The fp64 oracle as it stands, all host cores, on the same workload."""
     import numpy as np
@@ -546,6 +574,8 @@ def main():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--prefill-only", default=None, metavar="FMT,T,N,K",
                     help="time only this prefill case (e.g. q4k,4096,14336,4096) and print its record")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="time only the pure-read kernel over 0.06-128 MB per launch and fit t = fixed + bytes / BW")
     ap.add_argument("--rows-only", action="store_true",
                     help="time only the row-materialisation cases (after --calibrate-copy if given) and print them")
     args = ap.parse_args()
@@ -564,6 +594,10 @@ def main():
     if want != have:
         print(f"libqgemv.so build id {have} does not match the sources ({want}); rebuild", file=sys.stderr)
         sys.exit(3)
+
+    if args.ceiling_sweep:
+        print(json.dumps({"ceiling_sweep": measure_ceiling_sweep(), "build_id": have}), flush=True)
+        return
 
     if args.prefill_only:
         f, t, n, k = args.prefill_only.split(",")
