@@ -225,6 +225,49 @@ def test_gemv_deterministic_and_on_side_stream(q, fmt):
     assert np.array_equal(y0.view(np.uint64), y1.view(np.uint64))
 
 
+def test_gemv_concurrent_host_threads(q):
+    # the calls keep no global mutable state: four host threads, each with its
+    # own stream, format and buffers, enqueue 20 calls at once
+    import threading
+
+    cases = [("q4k", 3000, 4096), ("nvfp4", 2000, 14336), ("tq1", 5000, 4096), ("q4k", 777, 36864)]
+    data = []
+    for i, (fmt, n, k) in enumerate(cases):
+        w = synth.weights(fmt, n, k, synth.W_SEED + 400 + i)
+        x = synth.activations(fmt, k, synth.X_SEED + 400 + i)
+        ref = _run_gemv(q, fmt, w, x, n, k)  # one call alone, checked against the oracle
+        yr, ar = oracle.gemv(fmt, w, x, n, k)
+        _assert_close(fmt, n, k, ref, yr, ar)
+        data.append((fmt, n, k, _dev(w), _x_dev(x), ref))
+    outs = [[] for _ in cases]
+    errors = []
+
+    def work(j):
+        try:
+            fmt, n, k, wd, xd, _ = data[j]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    y = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+                    q.GEMV[fmt](wd, xd, y, n, k, s)
+                    outs[j].append(y)
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j, (fmt, n, k, _, _, ref) in enumerate(data):
+        assert len(outs[j]) == 20
+        for y in outs[j]:
+            assert np.array_equal(y.cpu().numpy().astype(np.float64), ref), (fmt, n, k)
+
+
 def test_gemv_empty_is_noop(q):
     y = torch.full((4,), 7.0, device=DEV)
     w = torch.zeros(144, dtype=torch.uint8, device=DEV)
