@@ -151,10 +151,12 @@ int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int6
  * K <= 2^20 and T <= 65535 * 128.  The weights are dequantised to the
  * activation type (one rounding per weight) and multiplied on the matrix
  * cores with fp32 accumulation.  Every element of y is overwritten.  When the
- * output has few 256 x 128 tiles the K range is split across workgroups whose
- * partial sums are added into y with fp32 atomics (after y is cleared on the
- * same stream), so the last bits can differ from run to run; the error bound
- * is unchanged.  T == 0 or M == 0 is a successful no-op; y must not overlap W
+ * output has fewer tiles (256 or 512 tokens x 128 rows) than the device has
+ * compute units, or 512-token tiles leave a last round of workgroups at most
+ * a quarter full, the K range of those tiles is split across workgroups whose
+ * partial sums are added into y with fp32 atomics (after their rows of y are
+ * cleared on the same stream), so the last bits can differ from run to run;
+ * the error bound is unchanged.  T == 0 or M == 0 is a successful no-op; y must not overlap W
  * or x. */
 int qgemm_q4k(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
               struct ihipStream_t* stream);
