@@ -204,7 +204,7 @@ struct Tq1Prefill {
   using T = _Float16;
   static constexpr bool kBf16 = false;
   static constexpr int kKMultiple = 256;
-  static constexpr int kLoads = 6;
+  static constexpr int kLoads = 3;
   struct Desc {
     __amdgpu_buffer_rsrc_t r;  // the tile's rows
     uint32_t row_bytes;
@@ -228,8 +228,14 @@ struct Tq1Prefill {
     const uint32_t al = a & ~3u;
     const uint32_t dead = live ? 0u : kPfDead;  // uniform
     Raw raw;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) raw.wd[i] = ld32s(d.r, al, dead + 4u * (uint32_t)i);
+    // the 20 bytes from the dword below the window: one dwordx4 and one
+    // dword load (dword-aligned, as multi-dword buffer loads require)
+    const u32x4 lo = ld128s(d.r, al, dead);
+    raw.wd[0] = lo.x;
+    raw.wd[1] = lo.y;
+    raw.wd[2] = lo.z;
+    raw.wd[3] = lo.w;
+    raw.wd[4] = ld32s(d.r, al, dead + 16u);
     raw.d = ld16s(d.r, blk + 52u, dead);
     raw.sh = (unsigned char)(a & 3u);
     return raw;
