@@ -229,7 +229,9 @@ struct Tq1Prefill {
     const uint32_t dead = live ? 0u : kPfDead;  // uniform
     Raw raw;
     // the 20 bytes from the dword below the window: one dwordx4 and one
-    // dword load (dword-aligned, as multi-dword buffer loads require)
+    // dword load (dword-aligned, as multi-dword buffer loads require; the
+    // range check is per dword, so the dwords of a qh window that lie past
+    // the tile's last row read as zero, and only its first two are used)
     const u32x4 lo = ld128s(d.r, al, dead);
     raw.wd[0] = lo.x;
     raw.wd[1] = lo.y;

@@ -70,21 +70,22 @@ __device__ __forceinline__ uint64_t load_le_a2(__amdgpu_buffer_rsrc_t r, uint32_
   return v;
 }
 
-// The same bytes from aligned dword loads, realigned with alignbyte (off is
-// 2-byte aligned): BYTES / 4 + 1 single-dword loads instead of BYTES / 2
-// 16-bit ones.  A dword wholly or partly past the range reads as zero, so
-// the bytes past the end of the range must not be needed.
+// The same bytes from the BYTES / 4 + 1 dwords around them, read with ONE
+// dword-aligned multi-dword load and realigned with alignbyte (off is 2-byte
+// aligned).  The range check is per dword: a dword wholly or partly past the
+// range reads as zero, so the bytes past the end of the range must not be
+// needed.
 template <int BYTES>
 __device__ __forceinline__ uint64_t load_le_a2_dw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   static_assert(BYTES == 4 || BYTES == 8, "4 or 8 bytes");
   const uint32_t al = off & ~3u, sh = off & 3u;
-  const unsigned d0 = ld32(r, al), d1 = ld32(r, al + 4u);
-  const unsigned lo = __builtin_amdgcn_alignbyte(d1, d0, sh);
   if constexpr (BYTES == 4) {
-    return lo;
+    const auto d = __builtin_amdgcn_raw_buffer_load_b64(r, (int)al, 0, 0);
+    return __builtin_amdgcn_alignbyte(d[1], d[0], sh);
   } else {
-    const unsigned d2 = ld32(r, al + 8u);
-    return (uint64_t)lo | ((uint64_t)__builtin_amdgcn_alignbyte(d2, d1, sh) << 32);
+    const auto d = __builtin_amdgcn_raw_buffer_load_b96(r, (int)al, 0, 0);
+    const unsigned lo = __builtin_amdgcn_alignbyte(d[1], d[0], sh);
+    return (uint64_t)lo | ((uint64_t)__builtin_amdgcn_alignbyte(d[2], d[1], sh) << 32);
   }
 }
 
