@@ -4,16 +4,24 @@
 One step = one Q4_K GEMV y = x . dequant(W)^T at N = 4096 rows, K = 14336 (the
 Llama-8B down-projection shape) on synthetic seeded weights, i.e. every row of
 the hot path: weight stream, activation staging, block decode, factored dot,
-reductions, store.  Inputs are resident in HBM before the timed region.  Each
-step reads a different one of R copies of the weights (R * 33 MB well above
-the 256 MB Infinity Cache), so every launch streams its weights from HBM.
+reductions, store.  Inputs are resident in HBM before the timed region.
+
+The timed region is ONE replay of a captured HIP graph of exactly --steps
+dependent launches; launch i reads weight copy i mod C with C = max(16,
+min(steps, 32)) distinct copies (>= 529 MB, above the 256 MB Infinity Cache),
+so every launch streams its weights from HBM.  It is bracketed by HIP events
+on the launch stream and queued right behind a clock pre-roll (replays of the
+same graph for --preroll-ms) and --warmup replays of the same graph, all
+between two device synchronisations.  value, ms_per_step and the roofline
+come from that event time.
 
 Printed: ONE JSON line with the metric (achieved HBM GB/s of the kernel over
 the algorithmic bytes weights + x + y), the roofline object of the dominant
-kernel, the CPU baseline (the fp64 oracle on the host cores) and extra context
-(pure-read ceiling over the same bytes, the other formats' shapes, the dense
-bf16 GEMV of the same shape, the general output stage, row materialisation,
-prefill on the matrix cores and a Llama-8B per-token sweep).
+kernel, the CPU baseline (the fp64 oracle on the host cores, and on one) and
+extra context (pure-read ceiling over the same bytes, the other formats'
+shapes, the dense bf16 GEMV of the same shape, the general output stage, row
+materialisation, prefill on the matrix cores and a Llama-8B per-token sweep
+with its per-role breakdown).
 """
 from __future__ import annotations
 
@@ -69,11 +77,127 @@ def measured_traffic(build_id: str):
         return None
 
 
+VALU_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "gemv_valu_counters.md")
+CLOCK_GHZ = 2.4  # nominal peak engine clock of the part
+
+
+def valu_estimates(build_id: str) -> dict:
+    """Per-shape VALU figures from the committed rocprofv3 counter summary
+    (lines `valu <fmt>_<n>x<k>: insts_per_wave=A busy_cycles_per_simd=B`),
+    only if it was taken with this very build of the library."""
+    out = {}
+    try:
+        lines = open(VALU_SUMMARY).read().splitlines()
+    except OSError:
+        return out
+    bid = [ln.split(":", 1)[1].strip() for ln in lines if ln.startswith("valu_build_id:")]
+    if not bid or bid[0] != build_id:
+        return out
+    for ln in lines:
+        if not ln.startswith("valu ") or ":" not in ln:
+            continue
+        key, rest = ln[len("valu "):].split(":", 1)
+        try:
+            vals = dict(kv.split("=") for kv in rest.split())
+            out[key.strip()] = {k: float(v) for k, v in vals.items()}
+        except ValueError:
+            continue
+    return out
+
+
+def valu_fields(valu: dict, fmt: str, n: int, k: int, us: float) -> dict:
+    """Estimated VALU issue share of one launch: the SIMD-cycles the counters
+    saw spent issuing VALU instructions, per SIMD, over the launch's cycles at
+    the nominal clock (empty when no summary of this build covers the shape)."""
+    v = valu.get(f"{fmt}_{n}x{k}")
+    if not v or "busy_cycles_per_simd" not in v:
+        return {}
+    return {"valu_insts_per_wave": round(v.get("insts_per_wave", float("nan")), 1),
+            "est_valu_issue_pct": round(100 * v["busy_cycles_per_simd"] / (us * 1e-6 * CLOCK_GHZ * 1e9), 1)}
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
+# Timed region: ONE captured HIP graph of exactly `steps` dependent launches
+# (launch i reads weight copy i mod `copies`), replayed once between two HIP
+# events on the launch stream.  Before it, on the same stream and with no
+# synchronisation in between: a clock pre-roll (replays of the same graph for
+# at least `preroll_ms`; the part's clocks ramp up over the first ~0.75 ms of
+# work after an idle gap) and `warmup` replays of the graph.  A device
+# synchronisation brackets the whole sequence.
+PREROLL_MS = 20.0
+
+
+def copies_for(steps: int, max_copies: int = 32) -> int:
+    """Distinct weight copies a timed graph cycles through: every launch of a
+    run of up to 16 consecutive ones reads its own copy (>= 16 x the bytes of
+    one launch, well above the 256 MB Infinity Cache for the 33 MB shapes)."""
+    return max(16, min(steps, max_copies))
+
+
+def time_graph(launch, steps, copies, warmup, stream, preroll_ms=PREROLL_MS, min_timed_ms=0.0, min_warm_ms=0.0,
+               reps=1):
+    """Per-launch device time of a graph of `steps` launches (launch(i, h)
+    enqueues launch i on stream handle h, i < copies).  Returns a dict: `us`
+    (event time of the timed replays / launches), `preroll_ms`, `replays`
+    (timed replays of the graph; 1 unless min_timed_ms asks for more),
+    `warmup_replays` and `wall_ms` (host time between the two
+    synchronisations, pre-roll and warm-up included).  `reps` timed replays
+    (default one) are queued back to back."""
+    import math
+
+    import torch
+
+    h = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        for i in range(copies):  # first touch of every copy, outside the graph
+            launch(i, h)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            launch(i % copies, h)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = max(e0.elapsed_time(e1), 1e-3)  # ms per replay, a first estimate
+    n_pre = math.ceil(preroll_ms / per) if preroll_ms > 0 else 0
+    warm = max(warmup, math.ceil(min_warm_ms / per)) if min_warm_ms > 0 else warmup
+    reps = max(reps, math.ceil(min_timed_ms / per)) if min_timed_ms > 0 else max(1, reps)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    p0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(n_pre):
+            g.replay()
+    p1.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            g.replay()
+    ev0.record(stream)  # right behind the warm-up: no idle gap before the timed launches
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {"us": 1e3 * ev0.elapsed_time(ev1) / (reps * steps), "preroll_ms": p0.elapsed_time(p1),
+           "replays": reps, "warmup_replays": warm, "wall_ms": 1e3 * wall}
+    del g
+    return res
+
+
+def measure_gpu(fmt, n, k, steps, warmup, preroll_ms=PREROLL_MS, with_ceiling=True):
+    """One GEMV shape: a graph of `steps` launches over copies_for(steps)
+    weight copies (and the pure-read kernel over the same bytes and copies)."""
     import numpy as np
     import torch
 
@@ -83,96 +207,25 @@ def measure_gpu(fmt, n, k, steps, warmup, rotate, launch, with_ceiling=True):
     seed = CASE_SEED.get((fmt, n, k), 9)
     w_host = synth.weights(fmt, n, k, synth.W_SEED + seed)
     x_host = synth.activations(fmt, k, synth.X_SEED + seed)
+    copies = copies_for(steps)
     w0 = torch.from_numpy(w_host).to(dev)
-    ws = [w0] + [w0.clone() for _ in range(rotate - 1)]
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     x = torch.from_numpy(x_host.view(np.int16).copy()).to(dev)
     y = torch.empty(n, dtype=torch.float32, device=dev)
     fn = qgemv.GEMV[fmt]
     stream = torch.cuda.Stream()
-    s_handle = stream.cuda_stream
     nbytes = algorithmic_bytes(fmt, n, k)
 
-    def one(i):
-        fn(ws[i % rotate], x, y, n, k, s_handle)
-
-    with torch.cuda.stream(stream):
-        for i in range(rotate):  # first touch of every copy
-            one(i)
-    torch.cuda.synchronize()
-
-    graph = None
-    if launch == "graph":
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(rotate):
-                one(i)
-        torch.cuda.synchronize()
-        # the untimed warm-up steps, as replays of the same graph right before
-        # the timed region (the GPU leaves its idle state before timing starts)
-        with torch.cuda.stream(stream):
-            for _ in range(max(1, warmup // rotate)):
-                graph.replay()
-        torch.cuda.synchronize()
-    else:
-        with torch.cuda.stream(stream):
-            for i in range(warmup):
-                one(i)
-        torch.cuda.synchronize()
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    with torch.cuda.stream(stream):
-        if graph is not None:
-            for _ in range(steps // rotate):
-                graph.replay()
-            for i in range(steps % rotate):
-                one(i)
-        else:
-            for i in range(steps):
-                one(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
-    res = {
-        "wall_s": wall,
-        "event_ms": ev_ms,
-        "us_per_launch_event": 1e3 * ev_ms / steps,
-        "us_per_step_wall": 1e6 * wall / steps,
-        "bytes": nbytes,
-    }
-    res["gbps_event"] = nbytes / (res["us_per_launch_event"] * 1e-6) / 1e9
-    res["gbps_wall"] = nbytes / (res["us_per_step_wall"] * 1e-6) / 1e9
-
+    t = time_graph(lambda i, h: fn(ws[i], x, y, n, k, h), steps, copies, warmup, stream, preroll_ms)
+    res = {"us": t["us"], "bytes": nbytes, "copies": copies, "preroll_ms": t["preroll_ms"],
+           "wall_ms": t["wall_ms"], "gbps": nbytes / (t["us"] * 1e-6) / 1e9}
     if with_ceiling:
         wb = synth.weight_bytes(fmt, n, k)
         sink = torch.empty(qgemv.qgemv_read_sink_len(wb), dtype=torch.float32, device=dev)
-        cg = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for i in range(rotate):
-                qgemv.qgemv_read_ceiling(ws[i], wb, sink, s_handle)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(cg, stream=stream):
-            for i in range(rotate):
-                qgemv.qgemv_read_ceiling(ws[i], wb, sink, s_handle)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            for _ in range(max(1, warmup // rotate)):
-                cg.replay()
-        reps = max(1, steps // rotate)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        with torch.cuda.stream(stream):
-            for _ in range(reps):
-                cg.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * ev0.elapsed_time(ev1) / (reps * rotate)
-        res["ceiling_us"] = us
-        res["ceiling_gbps"] = wb / (us * 1e-6) / 1e9
+        c = time_graph(lambda i, h: qgemv.qgemv_read_ceiling(ws[i], wb, sink, h), steps, copies, warmup, stream,
+                       preroll_ms)
+        res["ceiling_us"] = c["us"]
+        res["ceiling_gbps"] = wb / (c["us"] * 1e-6) / 1e9
     del ws
     torch.cuda.empty_cache()
     return res
@@ -196,12 +249,14 @@ SWEEP_MIXES = {
 }
 
 
-def measure_sweep(mix: str, tokens: int, layers: int = 32):
+def measure_sweep(mix: str, tokens: int, warmup: int, layers: int = 32, preroll_ms=PREROLL_MS):
     """One token = the 225 GEMVs of a Llama-8B decode step, each layer with its
     own weight buffers (cloned on the device from one generated matrix per
     shape, so every launch reads cold bytes: ~2.9 GB for the mixed sweep),
     captured in one HIP graph and replayed per token.  A mix named "<mix>-fused"
-    stores Q/K/V and gate/up as concatenated matrices (129 launches)."""
+    stores Q/K/V and gate/up as concatenated matrices (129 launches).  The
+    breakdown times each role's launches alone (one graph of its 32 launches,
+    or of 16 launches of lm_head) and sums them per token."""
     import numpy as np
     import torch
 
@@ -227,38 +282,33 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
         for role, n, k in layer_shapes:
             fmt = fmt_of[role]
             w = proto[(fmt, n, k)].clone()
-            calls.append((fmt, w, xs[(fmt, n, k)], torch.empty(n, dtype=torch.float32, device=dev), n, k))
+            calls.append((role, fmt, w, xs[(fmt, n, k)], torch.empty(n, dtype=torch.float32, device=dev), n, k))
             total_bytes += algorithmic_bytes(fmt, n, k)
     role, n, k = LLAMA8B_HEAD
     fmt = fmt_of[role]
-    calls.append((fmt, proto[(fmt, n, k)], xs[(fmt, n, k)], torch.empty(n, dtype=torch.float32, device=dev), n, k))
+    calls.append((role, fmt, proto[(fmt, n, k)], xs[(fmt, n, k)], torch.empty(n, dtype=torch.float32, device=dev), n, k))
     total_bytes += algorithmic_bytes(fmt, n, k)
     stream = torch.cuda.Stream()
-    h = stream.cuda_stream
 
-    def token():
-        for fmt, w, x, y, n, k in calls:
-            qgemv.GEMV[fmt](w, x, y, n, k, h)
+    def call(c, h):
+        _, fmt, w, x, y, n, k = c
+        qgemv.GEMV[fmt](w, x, y, n, k, h)
 
-    with torch.cuda.stream(stream):
-        token()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        token()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            g.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(tokens):
-            g.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    us = 1e3 * ev0.elapsed_time(ev1) / tokens
+    t = time_graph(lambda i, h: call(calls[i], h), len(calls), len(calls), warmup, stream, preroll_ms, reps=tokens)
+    us = t["us"] * len(calls)
+    breakdown, summed = {}, 0.0
+    for role, n, k in layer_shapes + [LLAMA8B_HEAD]:
+        mine = [c for c in calls if c[0] == role]
+        per_token = len(mine)
+        if len(mine) == 1:  # lm_head: one 296 MB matrix, larger than the Infinity Cache
+            mine = mine * 16
+        r = time_graph(lambda i, h: call(mine[i], h), len(mine), len(mine), warmup, stream, preroll_ms)
+        fmt = fmt_of[role]
+        b = algorithmic_bytes(fmt, n, k)
+        breakdown[role] = {"format": fmt, "rows": n, "k": k, "launches_per_token": per_token,
+                           "us_per_launch": round(r["us"], 3), "us_per_token": round(r["us"] * per_token, 2),
+                           "gbps": round(b / (r["us"] * 1e-6) / 1e9, 1)}
+        summed += r["us"] * per_token
     res = {
         "workload": f"Llama-8B decode step, {len(calls)} GEMVs ({layers} layers + lm_head), formats: {mix}"
                     + (", Q/K/V and gate/up as concatenated matrices" if fused else ""),
@@ -267,63 +317,16 @@ def measure_sweep(mix: str, tokens: int, layers: int = 32):
         "us_per_token": round(us, 2),
         "gbps": round(total_bytes / (us * 1e-6) / 1e9, 1),
         "pct_of_hbm_peak": round(100 * total_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
-        "tokens_timed": tokens,
+        "tokens_timed": t["replays"],
+        "breakdown": breakdown,
+        "breakdown_sum_us": round(summed, 2),
     }
-    del calls, proto, xs, g
+    del calls, proto, xs
     torch.cuda.empty_cache()
     return res
 
 
-def time_graph(launch, count, steps, warmup, stream, min_warm_ms=0.0, min_timed_ms=0.0):
-    """Average microseconds of one of `count` distinct launches (launch(i, h)
-    enqueues number i on stream handle h), captured together in one HIP graph
-    and replayed; every copy first touched once, eagerly, and the timed
-    replays queued right behind the warm-up replays.  With min_warm_ms /
-    min_timed_ms the warm-up and the timed region also last at least that
-    long (long kernels: the clocks take several ms of load to settle)."""
-    import math
-
-    import torch
-
-    h = stream.cuda_stream
-    with torch.cuda.stream(stream):
-        for i in range(count):
-            launch(i, h)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(count):
-            launch(i, h)
-    torch.cuda.synchronize()
-    warm_reps, reps = max(1, warmup // count), max(1, steps // count)
-    if min_warm_ms > 0 or min_timed_ms > 0:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        with torch.cuda.stream(stream):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per = max(e0.elapsed_time(e1), 1e-3)  # ms per replay
-        warm_reps = max(warm_reps, math.ceil(min_warm_ms / per))
-        reps = max(reps, math.ceil(min_timed_ms / per))
-    with torch.cuda.stream(stream):
-        for _ in range(warm_reps):
-            g.replay()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # no synchronize between the warm-up replays and the timed ones: after an
-    # idle gap the part's clocks ramp up again over the first ~0.75 ms of work
-    ev0.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(reps):
-            g.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    us = 1e3 * ev0.elapsed_time(ev1) / (reps * count)
-    del g
-    return us
-
-
-def measure_epilogue(steps, warmup, rotate):
+def measure_epilogue(steps, warmup, preroll_ms=PREROLL_MS):
     """The main Q4_K shape through the general output stage: fp16 y updated in
     place, y = v + 0.5 y (a residual-style accumulate), against the plain call."""
     import numpy as np
@@ -334,15 +337,17 @@ def measure_epilogue(steps, warmup, rotate):
     fmt, n, k, _ = MAIN
     dev = torch.device("cuda:0")
     seed = CASE_SEED[(fmt, n, k)]
+    copies = copies_for(steps)
     w0 = torch.from_numpy(synth.weights(fmt, n, k, synth.W_SEED + seed)).to(dev)
-    ws = [w0] + [w0.clone() for _ in range(rotate - 1)]
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     x = torch.from_numpy(synth.activations(fmt, k, synth.X_SEED + seed).view(np.int16).copy()).to(dev)
     y16 = torch.zeros(n, dtype=torch.float16, device=dev)
     y32 = torch.empty(n, dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
     us_ex = time_graph(lambda i, h: qgemv.qgemv_q4k_ex(ws[i], x, y16, n, k, 1.0, 0.5, y16, h),
-                       rotate, steps, warmup, stream)
-    us_plain = time_graph(lambda i, h: qgemv.qgemv_q4k(ws[i], x, y32, n, k, h), rotate, steps, warmup, stream)
+                       steps, copies, warmup, stream, preroll_ms)["us"]
+    us_plain = time_graph(lambda i, h: qgemv.qgemv_q4k(ws[i], x, y32, n, k, h), steps, copies, warmup, stream,
+                          preroll_ms)["us"]
     del ws
     torch.cuda.empty_cache()
     return {
@@ -362,9 +367,10 @@ ROWS_CASES = [
 ]
 
 
-def measure_rows(steps, warmup, rotate):
+def measure_rows(steps, warmup, preroll_ms=PREROLL_MS):
     """Row materialisation throughput: HBM bytes = packed bytes read + outputs
-    written (+ the int32 indices) per call."""
+    written (+ the int32 indices) per call.  A graph of `steps` launches cycles
+    through up to 1 GiB of weight copies and of output buffers."""
     import numpy as np
     import torch
 
@@ -374,7 +380,7 @@ def measure_rows(steps, warmup, rotate):
     out = {}
     for fmt, n, k, nsel, dtype, desc in ROWS_CASES:
         w0 = torch.from_numpy(synth.weights(fmt, n, k, 4100)).to(dev)
-        copies = max(1, min(rotate, (1 << 30) // w0.numel())) if nsel is None else 1
+        copies = max(1, min(copies_for(steps), (1 << 30) // w0.numel())) if nsel is None else 1
         ws = [w0] + [w0.clone() for _ in range(copies - 1)]
         rows = None
         nrows = n
@@ -388,8 +394,8 @@ def measure_rows(steps, warmup, rotate):
         os_ = [o] + [torch.empty_like(o) for _ in range(ocount - 1)]
         fn = qgemv.GET_ROWS[fmt]
         stream = torch.cuda.Stream()
-        us = time_graph(lambda i, h: fn(ws[i % copies], n, k, rows, nrows, os_[i % ocount], h), max(copies, 8),
-                        max(64, steps // 8), max(64, warmup // 8), stream)
+        us = time_graph(lambda i, h: fn(ws[i % copies], n, k, rows, nrows, os_[i % ocount], h), steps,
+                        max(copies, ocount), warmup, stream, preroll_ms)["us"]
         per_row = synth.weight_bytes(fmt, 1, k)
         nbytes = nrows * per_row + nrows * k * o.element_size() + (4 * nrows if rows is not None else 0)
         out[f"{fmt}_{n}x{k}_{nsel or 'all'}_{dtype}"] = {
@@ -443,8 +449,8 @@ def measure_prefill(steps, warmup, cases=None, unfused=True):
         x = torch.from_numpy(xs.view(np.int16)).to(dev)
         y = torch.empty((t, n), dtype=torch.float32, device=dev)
         fn = qgemv.GEMM[fmt]
-        us = time_graph(lambda i, h: fn(ws[i], x, y, t, n, k, h), 4, max(16, steps // 80), max(8, warmup // 80), stream,
-                        PREFILL_WARM_MS, PREFILL_TIMED_MS)
+        us = time_graph(lambda i, h: fn(ws[i], x, y, t, n, k, h), 4, 4, 0, stream, 0.0, PREFILL_TIMED_MS,
+                        PREFILL_WARM_MS)["us"]
         flops = 2.0 * t * n * k
         rec = {
             "workload": f"{fmt} prefill, {t} tokens x {n} rows x K {k}",
@@ -454,9 +460,8 @@ def measure_prefill(steps, warmup, cases=None, unfused=True):
         }
         if fmt == "q4k" and unfused:
             wf = torch.empty((n, k), dtype=torch.float16, device=dev)
-            us_rows = time_graph(lambda i, h: qgemv.qget_rows_q4k(ws[i], n, k, None, n, wf, h), 4,
-                                 max(16, steps // 80), max(8, warmup // 80), stream, PREFILL_WARM_MS,
-                                 PREFILL_TIMED_MS)
+            us_rows = time_graph(lambda i, h: qgemv.qget_rows_q4k(ws[i], n, k, None, n, wf, h), 4, 4, 0, stream,
+                                 0.0, PREFILL_TIMED_MS, PREFILL_WARM_MS)["us"]
             xf = x.view(torch.float16)
             with torch.cuda.stream(stream):  # first calls (library set-up) before the estimate
                 for _ in range(3):
@@ -494,7 +499,7 @@ def measure_prefill(steps, warmup, cases=None, unfused=True):
 
 def measure_ceiling_sweep():
     """Per-launch time of the pure-read kernel against the bytes it reads (a
-    graph of 32 launches over 32 buffers, as for the metric), and the least-
+    graph of 320 launches over 32 buffers, as for the metric), and the least-
     squares fit t = fixed + bytes / bandwidth over the launches of >= 4 MB:
     the fixed part is what one launch costs beyond streaming its bytes."""
     import numpy as np
@@ -509,7 +514,7 @@ def measure_ceiling_sweep():
         nbytes = int(mb * 1e6) // 16 * 16
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(32)]
         sink = torch.zeros(qgemv.qgemv_read_sink_len(nbytes), dtype=torch.float32, device=dev)
-        us = time_graph(lambda i, h: qgemv.qgemv_read_ceiling(bufs[i], nbytes, sink, h), 32, 3200, 1280, stream)
+        us = time_graph(lambda i, h: qgemv.qgemv_read_ceiling(bufs[i], nbytes, sink, h), 320, 32, 10, stream)["us"]
         points.append({"bytes": nbytes, "us": round(us, 3), "gbps": round(nbytes / us / 1e3, 1)})
         log(f"[bench] read {nbytes / 1e6:.3f} MB: {us:.3f} us/launch, {nbytes / us / 1e3:.1f} GB/s")
         del bufs, sink
@@ -520,8 +525,22 @@ def measure_ceiling_sweep():
     return {"points": points, "fit_fixed_us": round(float(fixed), 3), "fit_gbps": round(1e-3 / float(per_byte), 1)}
 
 
-def cpu_baseline(fmt, n, k, budget_s=10.0):
-    """The fp64 oracle as it stands, all host cores, on the same workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(fmt, n, k, budget_s=10.0, one_thread_rows=256):
+    """The fp64 oracle as it stands, on the same workload: all host cores on
+    the full matrix (median of repeated runs within about `budget_s` of CPU
+    time), and one thread on the first `one_thread_rows` rows."""
     import numpy as np
 
     import oracle
@@ -544,23 +563,45 @@ def cpu_baseline(fmt, n, k, budget_s=10.0):
         oracle.gemv(fmt, w, x, n, k)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
+    threads = oracle.threads()
+    # one thread on a row prefix: the same per-row work, scaled by its bytes
+    n1 = min(n, one_thread_rows)
+    if fmt == "nvfp4":  # nibbles [n][k/2], then scales [n][k/16]
+        nib, sc = w[: n * k // 2].reshape(n, -1), w[n * k // 2:].reshape(n, -1)
+        w1 = np.concatenate([nib[:n1].reshape(-1), sc[:n1].reshape(-1)])
+    else:
+        w1 = np.ascontiguousarray(w.reshape(n, -1)[:n1]).reshape(-1)
+    oracle.set_threads(1)
+    oracle.gemv(fmt, w1, x, n1, k)
+    t1s = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.gemv(fmt, w1, x, n1, k)
+        t1s.append(time.perf_counter() - t0)
+    t1 = statistics.median(t1s)
+    oracle.set_threads(cores)
     return {
         "value": algorithmic_bytes(fmt, n, k) / t / 1e9,
         "unit": "GB/s",
-        "cores": oracle.threads(),
+        "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"full {n}x{k} {fmt} matrix, median of {len(times)} runs "
                   f"({t * 1e3:.1f} ms each, fp64 scalar dequantise-then-dot, OpenMP over rows)",
+        "one_thread": {"value": algorithmic_bytes(fmt, n1, k) / t1 / 1e9, "unit": "GB/s",
+                       "sample": f"first {n1} rows of the same shape ({synth.weight_bytes(fmt, n1, k)} packed bytes), "
+                                 f"median of 3 runs ({t1 * 1e3:.1f} ms each)"},
     }
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3200)
-    ap.add_argument("--warmup", type=int, default=1280)
-    ap.add_argument("--rotate", type=int, default=32, help="distinct weight copies cycled through")
-    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--steps", type=int, default=320,
+                    help="launches in the timed graph (one replay of it is the timed region)")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed replays of that graph right before it")
+    ap.add_argument("--preroll-ms", type=float, default=PREROLL_MS,
+                    help="clock pre-roll: replays of the same graph for at least this long before the warm-up")
     ap.add_argument("--no-extra", action="store_true", help="skip the other formats' shapes")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", default="mixed,mixed-fused",
@@ -569,20 +610,25 @@ def main():
     ap.add_argument("--sweep-tokens", type=int, default=20)
     ap.add_argument("--fmt", default=None, help="measure only this format (q4k, nvfp4, tq1, f16, bf16) at N,K")
     ap.add_argument("--n", type=int, default=None)
+    ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 64 MiB device copy (a known-size reference for the HBM byte counters)")
-    ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--prefill-only", default=None, metavar="FMT,T,N,K",
                     help="time only this prefill case (e.g. q4k,4096,14336,4096) and print its record")
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="time only the pure-read kernel over 0.06-128 MB per launch and fit t = fixed + bytes / BW")
     ap.add_argument("--rows-only", action="store_true",
                     help="time only the row-materialisation cases (after --calibrate-copy if given) and print them")
+    ap.add_argument("--shapes-only", action="store_true",
+                    help="time only the GEMV shapes (main and other formats) with their read ceilings")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -615,7 +661,7 @@ def main():
         log("[bench] calibration: 8 copies of 64 MiB (read 65536 KiB + write 65536 KiB each)")
 
     if args.rows_only:
-        print(json.dumps({"get_rows": measure_rows(args.steps, args.warmup, args.rotate), "build_id": have}),
+        print(json.dumps({"get_rows": measure_rows(args.steps, args.warmup, args.preroll_ms), "build_id": have}),
               flush=True)
         return
 
@@ -623,22 +669,27 @@ def main():
     if args.fmt:
         fmt, n, k, desc = args.fmt, args.n or n, args.k or k, f"{args.fmt} GEMV M=1, N={args.n or n} x K={args.k or k}"
     log(f"[bench] build {have} on {torch.cuda.get_device_name(0)}; main {fmt} {n}x{k}")
-    main_res = measure_gpu(fmt, n, k, args.steps, args.warmup, args.rotate, args.launch)
-    log(f"[bench] main: {main_res['us_per_launch_event']:.3f} us/launch, {main_res['gbps_event']:.1f} GB/s "
-        f"(ceiling {main_res['ceiling_gbps']:.1f} GB/s)")
+    main_res = measure_gpu(fmt, n, k, args.steps, args.warmup, args.preroll_ms)
+    log(f"[bench] main: {main_res['us']:.3f} us/launch, {main_res['gbps']:.1f} GB/s "
+        f"(ceiling {main_res['ceiling_us']:.3f} us, {main_res['ceiling_gbps']:.1f} GB/s)")
 
+    valu = valu_estimates(have)
     extra = {}
     if not args.no_extra and not args.fmt:
         for efmt, en, ek, edesc in EXTRA:
-            r = measure_gpu(efmt, en, ek, max(args.rotate, args.steps // 4), args.warmup, args.rotate, args.launch)
-            extra[f"{efmt}_{en}x{ek}"] = {
+            r = measure_gpu(efmt, en, ek, args.steps, args.warmup, args.preroll_ms)
+            rec = {
                 "workload": edesc,
-                "us_per_gemv": round(r["us_per_launch_event"], 3),
-                "gbps": round(r["gbps_event"], 1),
-                "pct_of_hbm_peak": round(100 * r["gbps_event"] / HBM_PEAK_GBPS, 1),
+                "us_per_gemv": round(r["us"], 3),
+                "gbps": round(r["gbps"], 1),
+                "pct_of_hbm_peak": round(100 * r["gbps"] / HBM_PEAK_GBPS, 1),
+                "read_ceiling_us": round(r["ceiling_us"], 3),
                 "read_ceiling_gbps": round(r["ceiling_gbps"], 1),
+                "pct_of_read_ceiling": round(100 * r["ceiling_us"] / r["us"], 1),
             }
-            log(f"[bench] {efmt} {en}x{ek}: {r['us_per_launch_event']:.3f} us, {r['gbps_event']:.1f} GB/s")
+            rec.update(valu_fields(valu, efmt, en, ek, r["us"]))
+            extra[f"{efmt}_{en}x{ek}"] = rec
+            log(f"[bench] {efmt} {en}x{ek}: {r['us']:.3f} us, {r['gbps']:.1f} GB/s")
 
     fp4_vs_bf16 = None
     if "nvfp4_4096x14336" in extra and "bf16_4096x14336" in extra:
@@ -650,34 +701,35 @@ def main():
         log(f"[bench] NVFP4 vs bf16 at 4096x14336: {fp4_vs_bf16['speedup']}x")
 
     epilogue = rows_res = prefill_res = None
-    if not args.no_extra and not args.fmt:
-        epilogue = measure_epilogue(max(args.rotate, args.steps // 4), args.warmup, args.rotate)
-        log(f"[bench] epilogue: {epilogue['us_per_gemv']} us (plain {epilogue['us_per_gemv_plain_fp32']} us)")
-        rows_res = measure_rows(args.steps, args.warmup, args.rotate)
-        prefill_res = measure_prefill(args.steps, args.warmup)
-
     sweeps = {}
-    if not args.no_extra and not args.fmt and args.sweep != "none":
-        for mix in args.sweep.split(","):
-            r = measure_sweep(mix, args.sweep_tokens)
-            sweeps[mix] = r
-            log(f"[bench] sweep {mix}: {r['us_per_token']} us/token, {r['gbps']} GB/s over {r['gemvs_per_token']} GEMVs")
+    if not args.no_extra and not args.fmt and not args.shapes_only:
+        epilogue = measure_epilogue(args.steps, args.warmup, args.preroll_ms)
+        log(f"[bench] epilogue: {epilogue['us_per_gemv']} us (plain {epilogue['us_per_gemv_plain_fp32']} us)")
+        rows_res = measure_rows(args.steps, args.warmup, args.preroll_ms)
+        prefill_res = measure_prefill(args.steps, args.warmup)
+        if args.sweep != "none":
+            for mix in args.sweep.split(","):
+                r = measure_sweep(mix, args.sweep_tokens, args.warmup, preroll_ms=args.preroll_ms)
+                sweeps[mix] = r
+                log(f"[bench] sweep {mix}: {r['us_per_token']} us/token, {r['gbps']} GB/s over "
+                    f"{r['gemvs_per_token']} GEMVs (roles summed: {r['breakdown_sum_us']} us)")
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(fmt, n, k)
-        log(f"[bench] cpu oracle: {cpu['value']:.2f} GB/s on {cpu['cores']} threads")
+        log(f"[bench] cpu oracle: {cpu['value']:.2f} GB/s on {cpu['cores']} threads, "
+            f"{cpu['one_thread']['value']:.3f} GB/s on one")
 
-    value = main_res["gbps_wall"]
-    achieved = main_res["gbps_event"]
+    us = main_res["us"]
+    achieved = main_res["gbps"]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(achieved, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_res["us_per_step_wall"] / 1e3, 6),
+        "ms_per_step": round(us / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -687,8 +739,12 @@ def main():
             "workload": desc,
             "format": fmt, "n": n, "k": k,
             "algorithmic_bytes_per_gemv": main_res["bytes"],
-            "rotated_weight_copies": args.rotate,
-            "launch": "hipGraph of %d launches" % args.rotate if args.launch == "graph" else "eager",
+            "weight_copies": main_res["copies"],
+            "launch": (f"one HIP graph of {args.steps} dependent launches (launch i reads weight copy i mod "
+                       f"{main_res['copies']}), replayed once between two HIP events on its stream, right behind "
+                       f"{args.warmup} warm-up replays of the same graph"),
+            "clock_preroll_ms": round(main_res["preroll_ms"], 3),
+            "wall_ms_sync_to_sync": round(main_res["wall_ms"], 3),
         },
         "roofline": {
             "bound": "hbm",
@@ -698,10 +754,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(have) if (fmt, n, k) == MAIN[:3] else None,
         },
-        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "us_per_gemv": round(main_res["us_per_launch_event"], 3),
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "us_per_gemv": round(us, 3),
         "read_ceiling": {"gbps": round(main_res["ceiling_gbps"], 1), "us": round(main_res["ceiling_us"], 3),
-                         "note": "pure dwordx4 read of the same weight bytes, same rotation"},
+                         "pct_of_read_ceiling": round(100 * main_res["ceiling_us"] / us, 1),
+                         "note": "pure dwordx4 read of the same weight bytes, same graph and copies"},
+        "valu": valu_fields(valu, fmt, n, k, us),
         "cpu_baseline": cpu,
         "other_shapes": extra,
         "fp4_vs_bf16": fp4_vs_bf16,

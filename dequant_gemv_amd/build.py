@@ -22,10 +22,12 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build_id(defines=()) -> str:
+def build_id(defines=(), flags=()) -> str:
     h = hashlib.sha256()
     for d in defines:
         h.update(("-D" + d).encode())
+    for f in flags:
+        h.update(f.encode())
     files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [os.path.join(INCLUDE, "qgemv.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -34,16 +36,17 @@ def build_id(defines=()) -> str:
     return h.hexdigest()[:16]
 
 
-def build(verbose: bool = False, out_path: str = LIB, defines=()) -> str:
+def build(verbose: bool = False, out_path: str = LIB, defines=(), flags=()) -> str:
     """Compile every csrc/*.hip into one shared library.  `defines` (NAME=VALUE
-    strings) override the kernels' tuning constants; they enter the build id."""
+    strings) override the kernels' tuning constants and `flags` add compiler
+    options; both enter the build id."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     out = out_path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-fp32 VALU forms anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-result",
-           f"-DQGEMV_BUILD_ID=\"{build_id(defines)}\"", *("-D" + d for d in defines),
+           f"-DQGEMV_BUILD_ID=\"{build_id(defines, flags)}\"", *("-D" + d for d in defines), *flags,
            "-I", INCLUDE, "-I", CSRC, *sources(), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

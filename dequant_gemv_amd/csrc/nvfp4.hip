@@ -117,13 +117,16 @@ __global__ __launch_bounds__(64 * QGEMV_WG_WAVES) void nvfp4_gemv_kernel(const u
 #ifndef QGEMV_NVFP4_AHEAD
 #define QGEMV_NVFP4_AHEAD 4
 #endif
+#ifndef QGEMV_NVFP4_AHEAD0
+#define QGEMV_NVFP4_AHEAD0 QGEMV_NVFP4_AHEAD
+#endif
 #ifndef QGEMV_NVFP4_FIRST
-#define QGEMV_NVFP4_FIRST QGEMV_NVFP4_AHEAD
+#define QGEMV_NVFP4_FIRST 8  // loads issued right after the activation barrier (measured best of 4-12)
 #endif
 
 template <int KC, int R, int W>
 struct Nvfp4Rows {
-  using S = StreamSchedule<1024, R * KC, QGEMV_NVFP4_AHEAD, QGEMV_NVFP4_AHEAD, QGEMV_NVFP4_FIRST>;
+  using S = StreamSchedule<1024, R * KC, QGEMV_NVFP4_AHEAD0, QGEMV_NVFP4_AHEAD, QGEMV_NVFP4_FIRST>;
   static constexpr int kScLoads = (R * KC * 128 + 1023) / 1024;
   static constexpr int kStage = kScLoads * 1024 + S::kStage;
   static constexpr int kLds = W * kStage + KC * 4096;

@@ -223,13 +223,19 @@ __device__ __forceinline__ constexpr int q4k_xswz(int g) {
 #ifndef QGEMV_Q4K_AHEAD
 #define QGEMV_Q4K_AHEAD 3  // weight loads in flight per wave beyond the unit being consumed
 #endif
+#ifndef QGEMV_Q4K_AHEAD0
+#define QGEMV_Q4K_AHEAD0 QGEMV_Q4K_AHEAD  // weight loads issued before the activation barrier
+#endif
+#ifndef QGEMV_Q4K_FIRST
+#define QGEMV_Q4K_FIRST QGEMV_Q4K_AHEAD0  // weight loads issued before the first unit
+#endif
 
 template <int KC, int R, int W>
 struct Q4kRows {
   static constexpr int kUnitBytes = 8 * kQ4kBytes;  // 1152
   // Unit u = r*KC + ch; the schedule assumes the largest row record (8*KC
   // blocks), shorter records only end earlier.
-  using S = StreamSchedule<kUnitBytes, R * KC, QGEMV_Q4K_AHEAD, QGEMV_Q4K_AHEAD>;
+  using S = StreamSchedule<kUnitBytes, R * KC, QGEMV_Q4K_AHEAD0, QGEMV_Q4K_AHEAD, QGEMV_Q4K_FIRST>;
   static constexpr int kXBytes = KC * 4096;  // activations in LDS
   static constexpr int kLds = W * S::kStage + kXBytes;
   static_assert(KC >= 1 && KC <= 8, "K-chunk count");
@@ -257,17 +263,18 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_rows_kernel(const uint8_t* __
     return (uint32_t)(piece * 1024 + ((i & 32) + q4k_xswz(i & 31)) * 16);
   });
   const auto wr = make_rsrc(w + (int64_t)row0 * row_bytes, (uint32_t)(nrows * row_bytes));
-  stream_loads<0, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
+  stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX>(wr, stage, lane);
 
   const int bl = lane >> 3, p = lane & 7, c = p >> 1, h = p & 1;
   const Q4kScaleSel sel(c);
   const unsigned kOnes = 0x3C003C00u;
 
-  wait_vm<S::issued_before(0)>();  // this wave's activation pieces (issued before the weights) are in LDS
+  wait_vm<S::kUpFront>();  // this wave's activation pieces (issued before the weights) are in LDS
   __builtin_amdgcn_s_barrier();  // ... and every other wave's
   // the output stage's input for the wave's rows, after the barrier's wait
   // (the stream's later waits only get stricter by this one load)
   const auto pre = prefetch_rows(out, row0, nrows, lane);
+  stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
 
   // The lane's activations for every chunk, as fp16 pairs matching the masked
   // nibble layout, and their group sums (times 2^-24, see the K-split kernel).

@@ -99,7 +99,8 @@ __device__ __forceinline__ void store_rows(float (&acc)[R], const Out& out, type
 // kernel: up to 1024 rows one row per wave and 4 waves per workgroup (up to
 // one wave per SIMD); beyond, 8 waves (two per SIMD, so one wave's LDS
 // latency hides behind the other's arithmetic) and R = ceil(N / 2048), i.e.
-// about 256 workgroups that all run at once; past what RMAX (the largest R
+// about 256 workgroups that all run at once (R = 1, 2, 4, 7, 8, 10, 12, 14 or 16,
+// the smallest that covers N in one round); past what RMAX (the largest R
 // whose stage fits LDS at 8 waves) allows, R = min(4, RMAX) so that two
 // workgroups can share a CU and one's loads overlap the other's tail.
 // `launch(Int<R>{}, Int<W>{})` launches the instantiation.
@@ -120,6 +121,20 @@ hipError_t dispatch_rows(int64_t n, Launch&& launch) {
   }
   if constexpr (RMAX >= 8) {
     if (r8 <= 8) return launch(Int<8>{}, Int<8>{});
+  }
+  // still one round when the stages allow it (TQ1_0 rows are short: gate and
+  // up of Llama-8B as one 28672-row matrix take 14 rows per wave)
+  if constexpr (RMAX >= 10) {
+    if (r8 <= 10) return launch(Int<10>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 12) {
+    if (r8 <= 12) return launch(Int<12>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 14) {
+    if (r8 <= 14) return launch(Int<14>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 16) {
+    if (r8 <= 16) return launch(Int<16>{}, Int<8>{});
   }
   return launch(Int<(RMAX >= 4 ? 4 : RMAX >= 2 ? 2 : 1)>{}, Int<8>{});
 }

@@ -51,3 +51,23 @@ def test_committed_summary_is_parseable():
     fields = dict(line.split(":", 1) for line in open(bench.TRAFFIC_SUMMARY) if ":" in line)
     bid = fields["traffic_build_id"].strip()
     assert bench.measured_traffic(bid) == int(fields["traffic_bytes_per_launch"])
+
+
+def test_timed_graph_copies_exceed_the_infinity_cache():
+    # every run of up to 16 consecutive launches reads distinct copies; with
+    # the 33 MB metric shape that is >= 529 MB, above the 256 MB cache
+    assert bench.copies_for(1) == 16 and bench.copies_for(20) == 20 and bench.copies_for(3200) == 32
+    per = bench.algorithmic_bytes(*bench.MAIN[:3])
+    assert bench.copies_for(20) * per > 2 * 256e6
+
+
+def test_valu_fields_only_from_a_summary_of_the_same_build(tmp_path, monkeypatch):
+    p = tmp_path / "valu.md"
+    p.write_text("valu_build_id: abc\nvalu q4k_4096x14336: insts_per_wave=1200 busy_cycles_per_simd=9600\n")
+    monkeypatch.setattr(bench, "VALU_SUMMARY", str(p))
+    v = bench.valu_estimates("abc")
+    f = bench.valu_fields(v, "q4k", 4096, 14336, 8.0)
+    # 9600 SIMD-cycles of VALU issue in an 8 us launch at 2.4 GHz = 50%
+    assert f == {"valu_insts_per_wave": 1200.0, "est_valu_issue_pct": 50.0}
+    assert bench.valu_fields(bench.valu_estimates("other"), "q4k", 4096, 14336, 8.0) == {}
+    assert bench.valu_fields(v, "tq1", 14336, 4096, 8.0) == {}
