@@ -125,6 +125,73 @@ def bf16_weights(n: int, k: int, seed: int, sigma: float = 0.02) -> np.ndarray:
     return bits.view(np.uint8).reshape(n, 2 * k).copy()
 
 
+# ---- exact-arithmetic inputs ------------------------------------------------
+# Weights and activations whose every product and every partial sum is exact
+# in fp32, in any summation order (as long as sum_i |x_i| |w_i| stays below
+# 2^24 units of the finest product): the GEMV then has exactly one correct
+# fp32 result per row.  Scale factors are powers of two, activations are -1,
+# 0 or +1.  Only byte patterns are drawn here.
+
+F16_POW2 = {-2: 0x3400, -1: 0x3800, 0: 0x3C00, 1: 0x4000}  # fp16 codes of 2^e
+E4M3_POW2 = (0x28, 0x30, 0x38, 0x40, 0x48)  # OCP E4M3 codes of 2^-2 .. 2^2
+
+
+def x_ternary(fmt: str, k: int, seed: int) -> np.ndarray:
+    """Activations -1, 0 or +1 (equally likely) as fp16 or bf16 codes."""
+    one = 0x3F80 if x_dtype(fmt) == "bf16" else 0x3C00
+    t = _rng(seed).integers(-1, 2, size=k)
+    return np.where(t == 0, 0, np.where(t > 0, one, one | 0x8000)).astype(np.uint16)
+
+
+def q4k_weights_exact(n: int, k: int, seed: int, small: bool = False) -> np.ndarray:
+    """Q4_K matrix with d = dmin = 1.0; scale bytes and nibbles uniform, or
+    (small) every 6-bit scale and min below 16 (bytes 0-7 masked to their low
+    nibble, whose top two bits feed groups 4-7)."""
+    blk = q4k_weights(n, k, seed).reshape(n, k // QK, Q4K_BLOCK_BYTES)
+    blk[:, :, 0:4] = np.frombuffer(np.uint16(F16_POW2[0]).tobytes() * 2, dtype=np.uint8)
+    if small:
+        blk[:, :, 4:12] &= 0x0F
+    return blk.reshape(n, -1)
+
+
+def nvfp4_weights_exact(n: int, k: int, seed: int) -> np.ndarray:
+    """NVFP4 matrix with nibbles uniform and every scale a power of two in
+    [1/4, 4], its sign bit random (the format ignores it)."""
+    rng = _rng(seed)
+    nib = rng.integers(0, 256, size=n * k // 2, dtype=np.uint8)
+    sc = np.array(E4M3_POW2, dtype=np.uint8)[rng.integers(0, len(E4M3_POW2), size=n * k // NVFP4_SF)]
+    sc |= (rng.integers(0, 2, size=sc.size) << 7).astype(np.uint8)
+    return np.concatenate([nib, sc])
+
+
+def tq1_weights_exact(n: int, k: int, seed: int) -> np.ndarray:
+    """TQ1_0 matrix with trits uniform and d = +-2^e, e in -2..1."""
+    blk = tq1_weights(n, k, seed).reshape(n, k // QK, TQ1_BLOCK_BYTES)
+    rng = _rng(seed + 1)
+    codes = np.array(list(F16_POW2.values()), dtype=np.uint16)[rng.integers(0, len(F16_POW2), size=blk.shape[:2])]
+    codes |= (rng.integers(0, 2, size=codes.shape) << 15).astype(np.uint16)
+    blk[:, :, 52:54] = codes.view(np.uint8).reshape(n, k // QK, 2)
+    return blk.reshape(n, -1)
+
+
+def dense_weights_exact(fmt: str, n: int, k: int, seed: int) -> np.ndarray:
+    """Dense fp16 / bf16 matrix of integers -8..8 (exact in both types)."""
+    v = _rng(seed).integers(-8, 9, size=(n, k)).astype(np.float32)
+    if fmt == "f16":
+        return v.astype(np.float16).view(np.uint8).reshape(n, 2 * k)
+    return (v.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(n, 2 * k)
+
+
+def weights_exact(fmt: str, n: int, k: int, seed: int, small: bool = False) -> np.ndarray:
+    if fmt == "q4k":
+        return q4k_weights_exact(n, k, seed, small)
+    if fmt == "nvfp4":
+        return nvfp4_weights_exact(n, k, seed)
+    if fmt == "tq1":
+        return tq1_weights_exact(n, k, seed)
+    return dense_weights_exact(fmt, n, k, seed)
+
+
 def weights(fmt: str, n: int, k: int, seed: int) -> np.ndarray:
     return {"q4k": q4k_weights, "nvfp4": nvfp4_weights, "tq1": tq1_weights,
             "f16": f16_weights, "bf16": bf16_weights}[fmt](n, k, seed)
