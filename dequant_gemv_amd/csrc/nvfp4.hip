@@ -154,9 +154,11 @@ __global__ __launch_bounds__(64 * W) void nvfp4_gemv_rows_kernel(const uint8_t* 
     return (uint32_t)(((piece >> 2) * 256 + i * 4 + (piece & 3)) * 16);
   });
   // The scale run, then the first nibble loads.  The run is nrows*K/16
-  // bytes, not always a multiple of 16, and a 16-byte load that crosses the
-  // end of the range reads as zero: its last 2..14 bytes are fetched again
-  // with exact 2-byte loads and written over the zeros once the piece is in.
+  // bytes, not always a multiple of 16.  Buffer loads check the range dword
+  // by dword: dwords past the end, and a dword the end cuts through, read as
+  // zero.  So the bytes of the run's last partial 16-byte piece (2..14 of
+  // them) are fetched again with exact 2-byte loads and written over what the
+  // 16-byte load left there once the piece is in.
   const uint32_t sc_len = (uint32_t)(nrows * kScRow);
   const uint32_t sc_full = sc_len & ~15u;
   const bool tail_lane = 2u * (uint32_t)lane < sc_len - sc_full;

@@ -8,10 +8,10 @@
   activation with zero gives the four-digit form (g_5 = 0, g_4 = y_3).
 * Section "Not applicable": doing the floor pair in fp16 is wrong for 17 of the
   1280 digits, byte 79 digit 3 among them (tests/golden).
-* Section 2's element order: for il < 10 the 16 elements 16 il .. 16 il + 15
-  are 16 consecutive bytes of qs[0..31] at digit il/2; for 10 <= il < 15,
-  qs[32..47] at digit il - 10; il = 15 is the qh tail.  The order inside the
-  qh tail is not on the page: elements 240 + 4k + m take digit k of qh[m]
+* Section 2's element order, restated as an index map: element 32 k + j is
+  digit k of qs[j] (j < 32), element 160 + 16 k + i is digit k of qs[32 + i]
+  (i < 16), and the last 16 elements come from the qh tail.  The order inside
+  that tail is not on the page: elements 240 + 4k + m take digit k of qh[m]
   (parity unpinned for that order, a convention).
 """
 import os
