@@ -525,6 +525,68 @@ def measure_ceiling_sweep():
     return {"points": points, "fit_fixed_us": round(float(fixed), 3), "fit_gbps": round(1e-3 / float(per_byte), 1)}
 
 
+SIMDS = 1024  # 256 compute units x 4 SIMDs
+
+
+def counter_summary(dirs, shapes, build_id):
+    """Text summary of `rocprofv3 --pmc ... -- python3 bench.py ...` runs (the
+    counter_collection.csv files under `dirs`): per GEMV kernel, in the order
+    the run first dispatched them (one per entry of `shapes`), the median per
+    dispatch of every counter collected (cycle counters such as GRBM_GUI_ACTIVE
+    include the profiler's per-dispatch serialisation and are listed only).  FETCH_SIZE / WRITE_SIZE (KiB) are
+    scaled by what the same counter read for the run's first 8 copy dispatches
+    (--calibrate-copy: 64 MiB read + 64 MiB written each); the VALU counters
+    give instructions per wave and SIMD-cycles spent issuing VALU per SIMD
+    (SQ_ACTIVE_INST_VALU x 4 / SIMDs, the convention of rocprof's VALUBusy).
+    Returns the summary lines (those bench.py reads back included)."""
+    import csv
+    import glob
+
+    per = {}  # kernel name -> counter -> [values]
+    first = {}  # kernel name -> first dispatch id
+    copies = {}  # counter -> [values of copy dispatches, in dispatch order]
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                name, did = r["Kernel_Name"], int(r["Dispatch_Id"])
+                val = float(r["Counter_Value"])
+                if "copyBuffer" in name:
+                    copies.setdefault(r["Counter_Name"], []).append((did, val))
+                if "_gemv_" not in name:
+                    continue
+                per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(val)
+                first[name] = min(first.get(name, did), did)
+    names = sorted(per, key=first.get)
+    if len(names) != len(shapes):
+        raise SystemExit(f"{len(names)} GEMV kernels in the counter files, {len(shapes)} shapes expected")
+    scale = {}
+    for c, want_kib in (("FETCH_SIZE", 65536.0), ("WRITE_SIZE", 65536.0)):
+        vals = [v for _, v in sorted(copies.get(c, []))[:8]]
+        if len(vals) == 8 and statistics.median(vals) > 0:
+            scale[c] = want_kib / statistics.median(vals)
+    out = [f"valu_build_id: {build_id}" if any("SQ_INSTS_VALU" in per[n] for n in names) else
+           f"counters_build_id: {build_id}"]
+    for c, s in scale.items():
+        out.append(f"calibration {c}: copy of 64 MiB counts {65536.0 / s:.1f} KiB per dispatch, scale {s:.4f}")
+    for (fmt, n, k, _), name in zip(shapes, names):
+        cs = per[name]
+        med = {c: statistics.median(v) for c, v in cs.items()}
+        key = f"{fmt}_{n}x{k}"
+        out.append(f"kernel {key}: {name.split('(')[0]} ({len(next(iter(cs.values())))} dispatches)")
+        for c in sorted(med):
+            out.append(f"  {c}: {med[c]:.6g}")
+        if "FETCH_SIZE" in med and "WRITE_SIZE" in med and len(scale) == 2:
+            tb = int(round(1024 * (med["FETCH_SIZE"] * scale["FETCH_SIZE"] + med["WRITE_SIZE"] * scale["WRITE_SIZE"])))
+            ab = algorithmic_bytes(fmt, n, k)
+            out.append(f"traffic {key}: bytes_per_launch={tb} algorithmic={ab} ratio={tb / ab:.4f}")
+        if "SQ_INSTS_VALU" in med and "SQ_WAVES" in med:
+            line = f"valu {key}: insts_per_wave={med['SQ_INSTS_VALU'] / med['SQ_WAVES']:.1f}"
+            if "SQ_ACTIVE_INST_VALU" in med:
+                line += f" busy_cycles_per_simd={4 * med['SQ_ACTIVE_INST_VALU'] / SIMDS:.0f}"
+            out.append(line)
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -621,7 +683,19 @@ def main():
                     help="time only the row-materialisation cases (after --calibrate-copy if given) and print them")
     ap.add_argument("--shapes-only", action="store_true",
                     help="time only the GEMV shapes (main and other formats) with their read ceilings")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR", default=None,
+                    help="print a summary of rocprofv3 --pmc output directories of a run of this script with the "
+                         "same shape flags (--fmt/--n/--k, else the main and other shapes) and exit (no GPU used)")
     args = ap.parse_args()
+
+    if args.counter_summary:
+        from dequant_gemv_amd import build
+
+        shapes = [MAIN] if args.no_extra else [MAIN] + EXTRA
+        if args.fmt:
+            shapes = [(args.fmt, args.n or MAIN[1], args.k or MAIN[2], "")]
+        print("\n".join(counter_summary(args.counter_summary, shapes, build.build_id())))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "

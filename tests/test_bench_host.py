@@ -71,3 +71,51 @@ def test_valu_fields_only_from_a_summary_of_the_same_build(tmp_path, monkeypatch
     assert f == {"valu_insts_per_wave": 1200.0, "est_valu_issue_pct": 50.0}
     assert bench.valu_fields(bench.valu_estimates("other"), "q4k", 4096, 14336, 8.0) == {}
     assert bench.valu_fields(v, "tq1", 14336, 4096, 8.0) == {}
+
+
+def _counter_csv(path, rows):
+    cols = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+            "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+            "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w") as f:
+        f.write(",".join(f'"{c}"' for c in cols) + "\n")
+        for did, name, counter, val in rows:
+            f.write(f'{did},{did},"Agent 1",1,1,1,1024,1,"{name}",256,0,0,8,0,32,"{counter}",{val},0,1\n')
+
+
+def test_counter_summary_scales_by_the_copy_and_orders_kernels(tmp_path):
+    # two passes of a run over two shapes: FETCH_SIZE reads half of a copy's
+    # bytes (scale 2), WRITE_SIZE all of them; kernels in first-dispatch order
+    copy = "__amd_rocclr_copyBuffer"
+    ka, kb = "void qgemv::q4k_gemv_rows_kernel<7, 2, 8, qgemv::OutF32>(x)", "void qgemv::tq1_gemv_rows_kernel<1>(x)"
+    fetch = [(i, copy, "FETCH_SIZE", 32768.0) for i in range(1, 9)]
+    fetch += [(20, kb, "FETCH_SIZE", 999.0), (10, ka, "FETCH_SIZE", 16000.0), (11, ka, "FETCH_SIZE", 16400.0),
+              (12, ka, "FETCH_SIZE", 16100.0), (13, "void qgemv::read_ceiling_kernel(x)", "FETCH_SIZE", 5.0)]
+    write = [(i, copy, "WRITE_SIZE", 65536.0) for i in range(1, 9)]
+    write += [(10, ka, "WRITE_SIZE", 16.0), (20, kb, "WRITE_SIZE", 56.0)]
+    valu = [(10, ka, "SQ_INSTS_VALU", 2048 * 1200.0), (10, ka, "SQ_WAVES", 2048.0),
+            (10, ka, "SQ_ACTIVE_INST_VALU", 2048 * 1200.0), (10, ka, "GRBM_GUI_ACTIVE", 17280.0)]
+    _counter_csv(tmp_path / "f" / "h" / "r_counter_collection.csv", fetch)
+    _counter_csv(tmp_path / "w" / "h" / "r_counter_collection.csv", write + valu)
+    shapes = [("q4k", 4096, 14336, ""), ("tq1", 14336, 4096, "")]
+    out = bench.counter_summary([str(tmp_path / "f"), str(tmp_path / "w")], shapes, "bid")
+    assert out[0] == "valu_build_id: bid"
+    t = [ln for ln in out if ln.startswith("traffic q4k_4096x14336:")]
+    assert t == [f"traffic q4k_4096x14336: bytes_per_launch={1024 * (2 * 16100 + 16)} algorithmic=33075200 "
+                 f"ratio={1024 * (2 * 16100 + 16) / 33075200:.4f}"]
+    assert any(ln.startswith("traffic tq1_14336x4096: bytes_per_launch=" + str(1024 * (2 * 999 + 56))) for ln in out)
+    v = [ln for ln in out if ln.startswith("valu q4k_4096x14336:")]
+    assert v == ["valu q4k_4096x14336: insts_per_wave=1200.0 busy_cycles_per_simd=9600"]
+    # and bench.py reads its own valu lines back
+    p = tmp_path / "valu.md"
+    p.write_text("\n".join(out) + "\n")
+    old = bench.VALU_SUMMARY
+    try:
+        bench.VALU_SUMMARY = str(p)
+        est = bench.valu_estimates("bid")
+    finally:
+        bench.VALU_SUMMARY = old
+    assert est["q4k_4096x14336"]["busy_cycles_per_simd"] == 9600
+    f = bench.valu_fields(est, "q4k", 4096, 14336, 8.0)
+    assert f == {"valu_insts_per_wave": 1200.0, "est_valu_issue_pct": 50.0}
