@@ -80,6 +80,12 @@ __device__ __forceinline__ float pin_f32(float v) {
   return v;
 }
 
+// Makes v computed at this point of the program: a volatile asm keeps its
+// place among the other volatile asm statements (the memory fences and
+// counted waits), so arithmetic feeding v cannot sink past the next wait.
+__device__ __forceinline__ void settle(float& v) { __asm__ __volatile__("" : "+v"(v)); }
+__device__ __forceinline__ void settle(unsigned& v) { __asm__ __volatile__("" : "+v"(v)); }
+
 // v_dot2_f32_f16: a.x*b.x + a.y*b.y + c with fp32 accumulation.
 __device__ __forceinline__ float dot2h(unsigned a, unsigned b, float c) {
   return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
