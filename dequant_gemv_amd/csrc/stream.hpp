@@ -18,10 +18,18 @@ namespace qgemv {
 // load unit u depends on.  A CU's memory pipeline holds a bounded number of
 // requests and a wave issuing past that stalls at the load, holding back its
 // own arithmetic (and the barrier): hence the bounds.
-template <int UNIT_BYTES, int UNITS, int AHEAD0, int AHEAD, int FIRST = AHEAD0>
+//
+// With RING > 0 the stage is a ring of RING one-KiB slots (load i lands in
+// slot i % RING) instead of the whole run; a unit's 16-byte granules never
+// straddle the ring's end (units and slots are multiples of 16 bytes).  The
+// ring must hold every load issued while a unit's bytes are still unread:
+// the refill after unit u's wait reaches load issued_before(u + 1) - 1, unit
+// u starts at load first_load(u).
+template <int UNIT_BYTES, int UNITS, int AHEAD0, int AHEAD, int FIRST = AHEAD0, int RING = 0>
 struct StreamSchedule {
   static constexpr int kLoads = (UNITS * UNIT_BYTES + 1023) / 1024;
-  static constexpr int kStage = kLoads * 1024;
+  static constexpr int kRing = RING > 0 && RING < kLoads ? RING : kLoads;  // slots
+  static constexpr int kStage = kRing * 1024;
   static_assert(AHEAD >= (UNIT_BYTES + 1023) / 1024 + 1, "lookahead below one unit's loads");
   static_assert(AHEAD0 >= 1 && FIRST >= AHEAD0 && FIRST < 60 && AHEAD < 60, "vmcnt holds at most 63 outstanding loads");
   static constexpr int kUpFront = AHEAD0 < kLoads ? AHEAD0 : kLoads;  // issued before the barrier
@@ -36,17 +44,28 @@ struct StreamSchedule {
   }
   // vmcnt to wait for before consuming unit u (loads complete in issue order)
   static constexpr int wait_count(int u) { return issued_before(u) - 1 - last_load(u); }
+  static constexpr int first_load(int u) { return u * UNIT_BYTES / 1024; }
+  static constexpr bool ring_holds() {
+    if (issued_before(0) > kRing) return false;
+    for (int u = 0; u < UNITS; ++u)
+      if (issued_before(u + 1) - 1 - first_load(u) >= kRing) return false;
+    return true;
+  }
+  static_assert(ring_holds(), "the ring would overwrite bytes not yet read");
+  // LDS offset in the stage of byte b of the run
+  static constexpr int slot_offset(int b) { return b % kStage; }
 };
 
-// Issue loads [B, E) of a stream whose LDS stage starts at `stage`.
+// Issue loads [B, E) of a stream whose LDS stage starts at `stage` (a ring
+// of SLOTS one-KiB slots when the run is longer).
 // The group stays between the memory accesses before and after it (the
 // counted waits depend on the issue order of groups).
-template <int B, int E, int AUX>
+template <int B, int E, int AUX, int SLOTS = (1 << 30)>
 __device__ __forceinline__ void stream_loads(__amdgpu_buffer_rsrc_t r, unsigned char* stage, int lane) {
   compiler_fence();
   static_for<B, E>([&](auto i) {
     constexpr int I = decltype(i)::value;
-    ld128_lds<AUX>(r, stage + I * 1024, (uint32_t)(I * 1024 + 16 * lane));
+    ld128_lds<AUX>(r, stage + (I % SLOTS) * 1024, (uint32_t)(I * 1024 + 16 * lane));
   });
   compiler_fence();
 }

@@ -33,7 +33,7 @@
 // block; lanes fetch the d of the (at most two) blocks they touch with
 // ds_bpermute.  sum x*(t-1) = sum x*t - sum x, the second term precomputed.
 //
-// Digits from a table (the row-streaming kernel for K <= 4096 and more than
+// Digits from a table (the row-streaming kernel for K = 4096 and more than
 // 1024 rows): a 256-entry LDS table gives the five values digit_k(b) - 1 of a
 // byte as fp16 pairs, so a byte's five weights cost one 16-byte LDS read and
 // three v_dot2 instead of the arithmetic above (about 1 VALU instruction per
@@ -338,9 +338,10 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   store_rows<R>(acc, out, pre, row0, nrows, 1.f, lane);
 }
 
-// Table-driven row-streaming variant (K = 2048 or 4096, more than 1024
-// rows): the same run, stage and lanes as the row-streaming kernel above,
-// but the digits come from a table instead of arithmetic: entry b
+// Table-driven row-streaming variant (K = 4096, more than 1024 rows): the
+// same run and lanes as the row-streaming kernel above, the stage a ring of
+// eight one-KiB slots per wave (the lookahead never reaches further), and the
+// digits come from a table instead of arithmetic: entry b
 // (0..255) of the workgroup's digit table holds the fp16 values digit_k(b) - 1
 // (-1, 0 or +1, exact) as the pairs (k0, k1), (k2, k3), (k4, 0) and a zero
 // dword, so one 16-byte LDS read and three v_dot2_f32_f16 against the lane's
@@ -358,13 +359,17 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
 // needs are read from the stage.  A lane's 16 bytes touch at most two blocks
 // (a block boundary falls between byte pairs): the running sum is taken at the
 // boundary and each part is scaled by its block's d.
+#ifndef QGEMV_TQ1_RING
+#define QGEMV_TQ1_RING 8  // stage slots (one KiB each) per wave of the table-driven kernel
+#endif
+constexpr int kTq1Ring = QGEMV_TQ1_RING;
 #ifndef QGEMV_TQ1_PIPE
 #define QGEMV_TQ1_PIPE 1  // read a unit's table entries one unit ahead of its sums
 #endif
 
 template <int KS, int R, int W, int LREP>
 struct Tq1LutRows {
-  using S = StreamSchedule<kTq1SegBytes, R * KS, QGEMV_TQ1_AHEAD, QGEMV_TQ1_AHEAD, QGEMV_TQ1_FIRST>;
+  using S = StreamSchedule<kTq1SegBytes, R * KS, QGEMV_TQ1_AHEAD, QGEMV_TQ1_AHEAD, QGEMV_TQ1_FIRST, kTq1Ring>;
   static constexpr int kLutBytes = 256 * 16 * LREP;  // at LDS offset 0
   static constexpr int kXBytes = KS * 8192;
   static constexpr int kPairBytes = KS * 16 * 64 * 16;  // three activation pairs per (byte, lane) of a segment
@@ -377,7 +382,8 @@ struct Tq1LutRows {
 // LDS bytes of a row-streaming TQ1_0 launch (what the launcher checks
 // against the 160 KiB of a workgroup).
 constexpr int tq1_lut_lds(int ks, int r, int w, int lrep) {
-  return 256 * 16 * lrep + w * (((r * ks * kTq1SegBytes + 1023) / 1024) * 1024) + ks * 8192 + 16 + ks * 16 * 64 * 16;
+  const int loads = (r * ks * kTq1SegBytes + 1023) / 1024;
+  return 256 * 16 * lrep + w * (loads < kTq1Ring ? loads : kTq1Ring) * 1024 + ks * 8192 + 16 + ks * 16 * 64 * 16;
 }
 
 // fp16 bits of digit_k(b) - 1 for k = 0..4 (same recurrence as tq1_digits on
@@ -398,9 +404,11 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
                                                               const uint16_t* __restrict__ x,
                                                               Out out, int n, int nb) {
   using C = Tq1LutRows<KS, R, W, LREP>;
-  using S = typename C::S;  // assumes full segments; a short last segment only ends earlier
-  const int kRowBytes = nb * kTq1Bytes;
-  const int nbs_last = nb - (KS - 1) * kTq1SegBlocks;  // 8 or 16
+  using S = typename C::S;
+  // rows of KS full segments (nb == 16 KS, checked by the launcher): the
+  // run's unit offsets are compile-time constants
+  constexpr int kRowBytes = KS * kTq1SegBytes;
+  constexpr int nbs_last = kTq1SegBlocks;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
   unsigned char* const lut = lds;
   unsigned char* const xs = lds + C::kLutBytes + W * S::kStage;  // x, then a zero element
@@ -414,7 +422,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
   load_shared_pieces<8 * KS, W>(make_rsrc(x, (uint32_t)nb * 512u), xs, wave, lane,
                                 [](int piece, int i) { return (uint32_t)(piece * 1024 + 16 * i); });
   const auto wr = make_rsrc(w + (int64_t)row0 * kRowBytes, (uint32_t)(nrows * kRowBytes));
-  stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX>(wr, stage, lane);
+  stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
 
   // The digit table: thread t computes entry b = t % 256 and writes H = 64W /
   // 256 ... copies of it; copy (b + H j + t / 256) % LREP on step j, so the
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
   // the output stage's input for the wave's rows, after the barrier's wait
   // (the stream's later waits only get stricter by this one load)
   const auto pre = prefetch_rows(out, row0, nrows, lane);
-  stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX>(wr, stage, lane);
+  stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
   {
     unsigned xe[C::kSlots][5];
 #pragma unroll
@@ -530,11 +538,17 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
     wait_vm<S::wait_count(U)>();
     // refill first: the stage holds the whole run (no unread byte is
     // overwritten) and the arithmetic stays off the load path
-    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX>(wr, stage, lane);
-    const unsigned char* seg = stage + r * kRowBytes + sg * kTq1SegBytes;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(seg + o0);
-    const unsigned short db0 = *reinterpret_cast<const unsigned short*>(seg + dof0);
-    const unsigned short db1 = *reinterpret_cast<const unsigned short*>(seg + dof1);
+    stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
+    // the unit's bytes in the ring: its start plus the lane's offsets, less
+    // the ring's size past its end
+    constexpr int ub = S::slot_offset(r * kRowBytes + sg * kTq1SegBytes);
+    auto at = [&](int o) {
+      if constexpr (ub + kTq1SegBytes <= S::kStage) return stage + ub + o;
+      else return stage + (ub + o >= S::kStage ? ub + o - S::kStage : ub + o);
+    };
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(at(o0));
+    const unsigned short db0 = *reinterpret_cast<const unsigned short*>(at(dof0));
+    const unsigned short db1 = *reinterpret_cast<const unsigned short*>(at(dof1));
     in.d0 = slot0(sg) ? (float)__builtin_bit_cast(_Float16, db0) : 0.f;
     in.d1 = slot1(sg) ? (float)__builtin_bit_cast(_Float16, db1) : 0.f;
     const unsigned dw[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -725,6 +739,7 @@ static hipError_t launch_tq1_rows(const void* w, const void* x, const Out& y, in
 
 template <int KS, int R, int W, typename Out>
 static hipError_t launch_tq1_lut_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
+  if (k != (int64_t)KS * 4096) return hipErrorInvalidValue;  // full 16-block segments only
   constexpr int kLrep = QGEMV_TQ1_LREP == 16 && tq1_lut_lds(KS, R, W, 16) <= 160 * 1024 ? 16 : 8;
   static_assert(tq1_lut_lds(KS, R, W, kLrep) <= 160 * 1024, "LDS per workgroup");
   const int64_t rows_per_wg = (int64_t)W * R;
@@ -744,7 +759,7 @@ static hipError_t launch_tq1_lut(const void* w, const void* x, const Out& y, int
 
 #ifndef QGEMV_TQ1_IMPL
 #define QGEMV_TQ1_IMPL 2  // 1: K-split kernel only, 2: row-streaming for K % 2048 == 0, K <= 8192
-                          // (table-driven for K <= 4096 and more than 1024 rows)
+                          // (table-driven for K = 4096 and more than 1024 rows)
 #endif
 
 template <typename Out>
@@ -752,10 +767,12 @@ static hipError_t launch_tq1_gemv_out(const void* w, const void* x, const Out& y
                                       hipStream_t s) {
   if (QGEMV_TQ1_IMPL == 2 && k % 2048 == 0) {
     if (k <= 4096) {
-      // up to 1024 rows the arithmetic kernel (one row per wave, four waves
-      // per workgroup) starts faster than the table build pays off
-      if (n <= 1024) return launch_tq1_rows_r<1, 1, 4, Out>(w, x, y, n, k, s);
-      return launch_tq1_lut<1, Out>(w, x, y, n, k, s);
+      // K = 4096 over 1024 rows: the table-driven kernel; up to 1024 rows the
+      // arithmetic kernel (one row per wave, four waves per workgroup) starts
+      // faster than the table build pays off, and K = 2048 rows (half
+      // segments) stay with it too
+      if (k == 4096 && n > 1024) return launch_tq1_lut<1, Out>(w, x, y, n, k, s);
+      return launch_tq1_rows<1, Out>(w, x, y, n, k, s);
     }
     if (k <= 8192) return launch_tq1_rows<2, Out>(w, x, y, n, k, s);
   }

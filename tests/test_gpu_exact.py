@@ -52,9 +52,11 @@ def _cases():
     c += [("nvfp4", n, k) for k in (8224, 10272, 12320) for n in N_TWO]
     c += [("nvfp4", n, 14368) for n in (1000, 3001)]
     c += [("nvfp4", 4096, 14336), ("nvfp4", 1, 32), ("nvfp4", 3, 96), ("nvfp4", 33, 16416), ("nvfp4", 65, 36896)]
-    # TQ1_0: 16-block segments (K = 2048 is one short segment, 6144 ends in one)
+    # TQ1_0: 16-block segments (K = 2048 is one short segment, 6144 ends in one);
+    # K = 4096 over 1024 rows takes the table-driven kernel (every rows-per-wave
+    # choice, its ring-buffer stage from 10 rows per wave on)
     c += [("tq1", n, 2048) for n in N_ALL]
-    c += [("tq1", n, 4096) for n in (1000, 3001, 14336, 28672)]
+    c += [("tq1", n, 4096) for n in N_ALL + [14336, 28672]]
     c += [("tq1", n, k) for k in (6144, 8192) for n in N_SHORT + [19001, 23001]]
     c += [("tq1", 1, 256), ("tq1", 5, 768), ("tq1", 37, 4352), ("tq1", 33, 41216)]
     # dense fp16 / bf16
