@@ -118,8 +118,9 @@ __device__ __forceinline__ void store_rows(float (&acc)[R], const Out& out, type
 // kernel: up to 1024 rows one row per wave and 4 waves per workgroup (up to
 // one wave per SIMD); beyond, 8 waves (two per SIMD, so one wave's LDS
 // latency hides behind the other's arithmetic) and R = ceil(N / 2048), i.e.
-// about 256 workgroups that all run at once (R = 1, 2, 4, 7, 8, 10, 12, 14 or 16,
-// the smallest that covers N in one round); past what RMAX (the largest R
+// about 256 workgroups that all run at once (R = 1 to 8, 10, 12, 14 or 16,
+// the smallest that covers N in one round: a 6144-row matrix takes R = 3,
+// not 4, which would leave a quarter of the CUs idle); past what RMAX (the largest R
 // whose stage fits LDS at 8 waves) allows, R = min(4, RMAX) so that two
 // workgroups can share a CU and one's loads overlap the other's tail.
 // `launch(Int<R>{}, Int<W>{})` launches the instantiation.
@@ -130,10 +131,19 @@ hipError_t dispatch_rows(int64_t n, Launch&& launch) {
   const int64_t r8 = (n + 2047) / 2048;
   if (RMAX < 2 || r8 <= 1) return launch(Int<1>{}, Int<8>{});
   if constexpr (RMAX >= 2) {
-    if (RMAX < 4 || r8 <= 2) return launch(Int<2>{}, Int<8>{});
+    if (RMAX < 3 || r8 <= 2) return launch(Int<2>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 3) {
+    if (RMAX < 4 || r8 <= 3) return launch(Int<3>{}, Int<8>{});
   }
   if constexpr (RMAX >= 4) {
-    if (RMAX < 7 || r8 <= 4) return launch(Int<4>{}, Int<8>{});
+    if (RMAX < 5 || r8 <= 4) return launch(Int<4>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 5) {
+    if (RMAX < 6 || r8 <= 5) return launch(Int<5>{}, Int<8>{});
+  }
+  if constexpr (RMAX >= 6) {
+    if (RMAX < 7 || r8 <= 6) return launch(Int<6>{}, Int<8>{});
   }
   if constexpr (RMAX >= 7) {
     if (r8 <= 7) return launch(Int<7>{}, Int<8>{});

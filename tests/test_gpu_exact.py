@@ -27,10 +27,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 # rows that pick each rows-per-wave choice of the row-streaming launch (one
-# wave per SIMD, then 1, 2, 4, 7, 8, 10, 12, 14, 16 rows per wave, then more
-# than one round); the larger ones only where the LDS stage allows them
-N_ALL = [1000, 1500, 3001, 7001, 13001, 15001, 19001, 23001, 27001, 31001, 40001]
-N_SHORT = [1000, 1500, 3001, 7001, 13001, 15001, 17001]
+# wave per SIMD, then 1 to 8, 10, 12, 14, 16 rows per wave, then more than
+# one round); the larger ones only where the LDS stage allows them
+N_ALL = [1000, 1500, 3001, 5001, 7001, 9001, 11001, 13001, 15001, 19001, 23001, 27001, 31001, 40001]
+N_SHORT = [1000, 1500, 3001, 5001, 7001, 11001, 13001, 15001, 17001]
 N_FEW = [1000, 1500, 3001, 9001]
 N_TWO = [1000, 1500, 5001]
 
