@@ -683,6 +683,8 @@ def main():
                     help="time only the row-materialisation cases (after --calibrate-copy if given) and print them")
     ap.add_argument("--shapes-only", action="store_true",
                     help="time only the GEMV shapes (main and other formats) with their read ceilings")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="time only the Llama-8B decode sweeps (--sweep) and print them")
     ap.add_argument("--counter-summary", nargs="+", metavar="DIR", default=None,
                     help="print a summary of rocprofv3 --pmc output directories of a run of this script with the "
                          "same shape flags (--fmt/--n/--k, else the main and other shapes) and exit (no GPU used)")
@@ -737,6 +739,14 @@ def main():
     if args.rows_only:
         print(json.dumps({"get_rows": measure_rows(args.steps, args.warmup, args.preroll_ms), "build_id": have}),
               flush=True)
+        return
+
+    if args.sweep_only:
+        sweeps = {}
+        for mix in args.sweep.split(","):
+            sweeps[mix] = measure_sweep(mix, args.sweep_tokens, args.warmup, preroll_ms=args.preroll_ms)
+            log(f"[bench] sweep {mix}: {sweeps[mix]['us_per_token']} us/token")
+        print(json.dumps({"decode_sweep": sweeps, "build_id": have}), flush=True)
         return
 
     fmt, n, k, desc = MAIN
