@@ -458,6 +458,13 @@ def measure_prefill(steps, warmup, cases=None, unfused=True):
             "tflops": round(flops / us / 1e6, 1),
             "pct_of_mfma_peak": round(100 * flops / us / 1e6 / MFMA_PEAK_TFLOPS, 1),
         }
+        nws = qgemv.qgemm_workspace_bytes(t, n, k)
+        if nws:  # K split: the same call through a workspace (fixed addition order)
+            wsb = torch.empty(nws // 4, dtype=torch.float32, device=dev)
+            rec["workspace_us"] = round(time_graph(lambda i, h: qgemv.GEMM_WS[fmt](ws[i], x, y, t, n, k, wsb, h), 4, 4,
+                                                   0, stream, 0.0, PREFILL_TIMED_MS, PREFILL_WARM_MS)["us"], 2)
+            rec["workspace_mb"] = round(nws / 1e6, 1)
+            del wsb
         if fmt == "q4k" and unfused:
             wf = torch.empty((n, k), dtype=torch.float16, device=dev)
             us_rows = time_graph(lambda i, h: qgemv.qget_rows_q4k(ws[i], n, k, None, n, wf, h), 4, 4, 0, stream,

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "launch.hpp"
+#include "prefill_plan.hpp"
 #include "qgemv.h"
 
 #ifndef QGEMV_BUILD_ID
@@ -131,7 +132,10 @@ int get_rows(Fmt f, const void* w, int64_t m, int64_t k, const int32_t* rows, in
   }
 }
 
-int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, int64_t k, hipStream_t s) {
+// use_ws: the _ws entry points (K splits through the caller's workspace);
+// otherwise K splits add into y with atomics.
+int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, int64_t k, bool use_ws, void* ws,
+         int64_t ws_bytes, hipStream_t s) {
   int rc = check_shape(f, m, k);
   if (rc != QGEMV_OK) return rc;
   // the grid's y dimension counts tiles of 256 or 512 activation rows (at
@@ -141,12 +145,23 @@ int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, in
   if (t == 0 || m == 0) return QGEMV_OK;
   if (!w || !x || !y) return QGEMV_E_NULL;
   if (misaligned(w, 16) || misaligned(x, 16) || misaligned(y, 4)) return QGEMV_E_ALIGN;
-  const int64_t yb = t * m * 4;
-  if (overlap(y, yb, w, weight_bytes(f, m, k)) || overlap(y, yb, x, t * k * 2)) return QGEMV_E_ALIAS;
+  const int64_t yb = t * m * 4, wb = weight_bytes(f, m, k), xb = t * k * 2;
+  if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return QGEMV_E_ALIAS;
+  void* wsp = nullptr;
+  if (use_ws) {
+    const int64_t need = qgemv::prefill_workspace_bytes(t, m, k);
+    if (need > 0) {
+      if (!ws) return QGEMV_E_NULL;
+      if (misaligned(ws, 256)) return QGEMV_E_ALIGN;
+      if (ws_bytes < need) return QGEMV_E_WORKSPACE;
+      if (overlap(ws, need, y, yb) || overlap(ws, need, w, wb) || overlap(ws, need, x, xb)) return QGEMV_E_ALIAS;
+      wsp = ws;
+    }
+  }
   switch (f) {
-    case kQ4k: return finish(qgemv::launch_q4k_prefill(w, x, y, t, m, k, s));
-    case kNvfp4: return finish(qgemv::launch_nvfp4_prefill(w, x, y, t, m, k, s));
-    case kTq1: return finish(qgemv::launch_tq1_prefill(w, x, y, t, m, k, s));
+    case kQ4k: return finish(qgemv::launch_q4k_prefill(w, x, y, t, m, k, wsp, s));
+    case kNvfp4: return finish(qgemv::launch_nvfp4_prefill(w, x, y, t, m, k, wsp, s));
+    case kTq1: return finish(qgemv::launch_tq1_prefill(w, x, y, t, m, k, wsp, s));
     default: return QGEMV_E_SHAPE;
   }
 }
@@ -222,13 +237,31 @@ int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int6
 }
 
 int qgemm_q4k(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
-  return gemm(kQ4k, w, x, y, T, M, K, s);
+  return gemm(kQ4k, w, x, y, T, M, K, false, nullptr, 0, s);
 }
 int qgemm_nvfp4(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
-  return gemm(kNvfp4, w, x, y, T, M, K, s);
+  return gemm(kNvfp4, w, x, y, T, M, K, false, nullptr, 0, s);
 }
 int qgemm_tq1(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
-  return gemm(kTq1, w, x, y, T, M, K, s);
+  return gemm(kTq1, w, x, y, T, M, K, false, nullptr, 0, s);
+}
+
+int64_t qgemm_workspace_bytes(int64_t T, int64_t M, int64_t K) {
+  if (T < 0 || M < 0 || K <= 0 || T > 65535 * int64_t(128) || M > (int64_t(1) << 31) || K > qgemv::kPrefillMaxK)
+    return QGEMV_E_SHAPE;
+  return qgemv::prefill_workspace_bytes(T, M, K);
+}
+int qgemm_q4k_ws(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, void* ws, int64_t ws_bytes,
+                 struct ihipStream_t* s) {
+  return gemm(kQ4k, w, x, y, T, M, K, true, ws, ws_bytes, s);
+}
+int qgemm_nvfp4_ws(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, void* ws,
+                   int64_t ws_bytes, struct ihipStream_t* s) {
+  return gemm(kNvfp4, w, x, y, T, M, K, true, ws, ws_bytes, s);
+}
+int qgemm_tq1_ws(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, void* ws, int64_t ws_bytes,
+                 struct ihipStream_t* s) {
+  return gemm(kTq1, w, x, y, T, M, K, true, ws, ws_bytes, s);
 }
 
 int64_t qgemv_read_sink_len(int64_t bytes) { return bytes > 0 ? qgemv::read_sink_len(bytes) : 0; }
@@ -252,6 +285,7 @@ const char* qgemv_strerror(int code) {
     case QGEMV_E_HIP: return "the HIP runtime rejected the launch (see qgemv_last_hip_error)";
     case QGEMV_E_ALIAS: return "the output overlaps an input";
     case QGEMV_E_DTYPE: return "unknown element type (QGEMV_F32, QGEMV_F16 or QGEMV_BF16)";
+    case QGEMV_E_WORKSPACE: return "the workspace is smaller than qgemm_workspace_bytes asks for";
     default: return "unknown qgemv error code";
   }
 }

@@ -33,10 +33,15 @@ hipError_t launch_tq1_get_rows(const void* w, int64_t n, int64_t k, const int32_
                                int dtype, hipStream_t s);
 // Prefill: y[t][r] (fp32, [T][n]) = x[t] . dequant(W)[r] for T activation rows.
 constexpr int64_t kPrefillMaxK = int64_t(1) << 20;
-hipError_t launch_q4k_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s);
-hipError_t launch_nvfp4_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
+// Prefill; ws: NULL (K splits add into y with atomics) or a workspace of at
+// least prefill_workspace_bytes(t, n, k) bytes (prefill_plan.hpp) whose
+// counters are zero.
+hipError_t launch_q4k_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, void* ws,
+                              hipStream_t s);
+hipError_t launch_nvfp4_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, void* ws,
                                 hipStream_t s);
-hipError_t launch_tq1_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_tq1_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, void* ws,
+                              hipStream_t s);
 hipError_t launch_read_ceiling(const void* buf, int64_t bytes, float* sink, hipStream_t s);
 int64_t read_sink_len(int64_t bytes);
 

@@ -31,6 +31,7 @@
 
 #include "device.hpp"
 #include "launch.hpp"
+#include "prefill_plan.hpp"
 
 namespace qgemv {
 
@@ -38,8 +39,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPfBN = 128;    // weight rows per workgroup tile
-constexpr int kPfKS = 64;     // weights per K step
 constexpr int kPfRowB = 128;  // LDS bytes per tile row per step (64 16-bit values)
 constexpr int kPfWTile = kPfBN * kPfRowB;  // 16 KiB of weights per stage
 constexpr int kPfWaves = 8;
@@ -273,7 +272,7 @@ struct Tq1Prefill {
 // ---- the kernel ---------------------------------------------------------------
 
 constexpr int kPfWQ = 3;      // packed-weight register slots: loads run kPfWQ - 1 steps ahead of the decode
-constexpr int kPfUnroll = 6;  // steps per loop iteration (a multiple of XS, 2 and kPfWQ): indices are compile-time
+static_assert(kPfUnroll % kPfWQ == 0, "steps per loop iteration: a multiple of the weight register slots");
 
 // Step s, with XS activation stages: the activations of step s + XS - 1 are
 // copied into activation stage (s + XS - 1) % XS and the packed weights of
@@ -287,15 +286,28 @@ constexpr int kPfUnroll = 6;  // steps per loop iteration (a multiple of XS, 2 a
 // compile time (the loop runs kPfUnroll steps per iteration): the compiler
 // then knows that the copies in flight into one stage never alias the
 // fragment reads of another, and does not wait for them there.
+// Where the partial sums of a tile split over K go.  With part == nullptr
+// they are added into y with fp32 atomics (y cleared first).  Otherwise split
+// z of tile `tile` stores its whole BT x 128 partial tile at part + (tile *
+// nsplit + z) * BT * 128 (row-major, tile-local rows and columns), and
+// prefill_reduce_kernel, launched after it on the same stream, adds the
+// nsplit partials of every output in split order: the result does not vary
+// from run to run, and no workgroup waits for another.
+struct PfSplit {
+  float* part;
+  int tile;
+  int nsplit;
+};
+
 // One workgroup's tile: tokens t0 .. t0 + BT - 1, weight rows n0 .. n0 + 127,
 // K split z (steps [z * split_steps, ...)), with XS activation stages in the
 // LDS arrays xs0..xs2 (at least BT * 128 bytes each, xs2 used when XS = 3)
-// and the weight stages ws0, ws1; the partial sums are added into y with
-// atomics when `atomic` (a K split), stored otherwise.
+// and the weight stages ws0, ws1; the partial sums go where `sp` says when
+// `split` (a K split), they are stored otherwise.
 template <typename F, int BT, int XS>
 __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ w, const uint16_t* __restrict__ x,
                                              float* __restrict__ y, int t_count, int n, int k, int split_steps,
-                                             int t0, int n0, int z, bool atomic, unsigned char* xs0,
+                                             int t0, int n0, int z, bool split, PfSplit sp, unsigned char* xs0,
                                              unsigned char* xs1, unsigned char* xs2, unsigned char* ws0,
                                              unsigned char* ws1) {
   static_assert(BT == 256 || BT == 512, "256 or 512 tokens per tile");
@@ -443,6 +455,17 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ w, cons
 
   // D[m][n] of tile (i, j) sits at lane n + 32 ((m / 4) % 2), register
   // 4 (m / 8) + m % 4: register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4
+  if (split && sp.part) {
+    float* const mine = sp.part + ((int64_t)sp.tile * sp.nsplit + z) * ((int64_t)BT * kPfBN);
+#pragma unroll
+    for (int i = 0; i < kPfMI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          mine[(wt + 32 * i + 8 * (r >> 2) + 4 * fq + (r & 3)) * kPfBN + wn + 32 * j + fl] = acc[i][j][r];
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kPfMI; ++i)
 #pragma unroll
@@ -454,7 +477,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ w, cons
         for (int j = 0; j < 2; ++j) {
           const int col = n0 + wn + 32 * j + fl;
           if (col < n) {
-            if (!atomic)
+            if (!split)
               yr[col] = acc[i][j][r];
             else
               atomicAdd(yr + col, acc[i][j][r]);  // partial sum of one K split (y zeroed first)
@@ -468,15 +491,16 @@ template <typename F, int BT>
 __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_kernel(const uint8_t* __restrict__ w,
                                                                   const uint16_t* __restrict__ x,
                                                                   float* __restrict__ y, int t_count, int n,
-                                                                  int k, int split_steps) {
+                                                                  int k, int split_steps, float* part) {
   constexpr int XS = BT == 512 ? 2 : 3;  // as many activation stages as fit the LDS
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[BT * kPfRowB];
   __shared__ __attribute__((aligned(1024))) unsigned char xs1[BT * kPfRowB];
   __shared__ __attribute__((aligned(1024))) unsigned char xs2[XS == 3 ? BT * kPfRowB : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char ws0[kPfWTile];
   __shared__ __attribute__((aligned(1024))) unsigned char ws1[kPfWTile];
+  const PfSplit sp{part, (int)(blockIdx.y * gridDim.x + blockIdx.x), (int)gridDim.z};
   prefill_tile<F, BT, XS>(w, x, y, t_count, n, k, split_steps, blockIdx.y * BT, blockIdx.x * kPfBN, blockIdx.z,
-                          gridDim.z > 1, xs0, xs1, xs2, ws0, ws1);
+                          gridDim.z > 1, sp, xs0, xs1, xs2, ws0, ws1);
 }
 
 // 512-token tiles whose count leaves a last round at most a quarter full: the
@@ -490,7 +514,8 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_tail_kernel(const ui
                                                                        const uint16_t* __restrict__ x,
                                                                        float* __restrict__ y, int t_count, int n,
                                                                        int k, int row_tiles, int n_full,
-                                                                       int tail_split, int split_steps) {
+                                                                       int tail_split, int split_steps,
+                                                                       float* part) {
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[512 * kPfRowB];
   __shared__ __attribute__((aligned(1024))) unsigned char xs1[512 * kPfRowB];
   __shared__ __attribute__((aligned(1024))) unsigned char xs2[16];
@@ -503,8 +528,9 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_tail_kernel(const ui
     z = (b - n_full) % tail_split;
     ss = split_steps;
   }
+  const PfSplit sp{part, tile - n_full, tail_split};
   prefill_tile<F, 512, 2>(w, x, y, t_count, n, k, ss, (tile / row_tiles) * 512, (tile % row_tiles) * kPfBN, z,
-                          b >= n_full, xs0, xs1, xs2, ws0, ws1);
+                          b >= n_full, sp, xs0, xs1, xs2, ws0, ws1);
 }
 
 // Clears y[0 .. count): 16-byte stores from the first 16-byte boundary on,
@@ -526,85 +552,90 @@ __global__ __launch_bounds__(256) void prefill_zero_kernel(float* __restrict__ y
   }
 }
 
+// Sums the nsplit partial tiles of the split tiles into y, in split order:
+// partial tile p (p = 0 .. tiles - 1, bt x 128 outputs each) is output tile
+// first + p of the launch, whose token rows start at ((first + p) /
+// row_tiles) * bt and weight rows at ((first + p) % row_tiles) * 128.  A
+// workgroup of 256 threads takes 8 rows x 128 columns of one tile (thread i:
+// column i % 128, rows i / 128, + 2, + 4, + 6), so its loads and stores are
+// contiguous across the wave.  Launched with tiles * bt / 8 workgroups.
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const float* __restrict__ part, float* __restrict__ y,
+                                                             int t_count, int n, int bt, int row_tiles, int first,
+                                                             int nsplit) {
+  const int per_tile = bt / 8;
+  const int p = blockIdx.x / per_tile, r8 = (blockIdx.x % per_tile) * 8;
+  const int tile = first + p;
+  const int t0 = (tile / row_tiles) * bt, n0 = (tile % row_tiles) * kPfBN;
+  const int c = threadIdx.x & 127;
+  const int64_t tile_f = (int64_t)bt * kPfBN;
+  const float* const src = part + (int64_t)p * nsplit * tile_f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = r8 + (threadIdx.x >> 7) + 2 * j;
+    float v = 0.f;
+    for (int z = 0; z < nsplit; ++z) v += src[z * tile_f + (int64_t)r * kPfBN + c];
+    const int t = t0 + r, col = n0 + c;
+    if (t < t_count && col < n) y[(int64_t)t * n + col] = v;
+  }
+}
+
 // Tiles of 256 or 512 tokens x 128 rows, one workgroup per CU.  When there are
 // fewer tiles than CUs, K is split as well (one round of workgroups, at
-// least 8 steps per split) and the splits add their partial sums into y with
-// fp32 atomics, y being cleared by a fill kernel first (a kernel, so that the
-// sequence can be captured in a graph); the order of those few additions
-// varies from run to run.  When 512-token tiles leave a last round at most
-// a quarter full, only the tiles of that round are split (prefill_tail_kernel).
+// least 8 steps per split); when 512-token tiles leave a last round at most a
+// quarter full, only the tiles of that round are split (prefill_tail_kernel).
+// The splits' partial sums either go to a workspace and a second kernel adds
+// them in a fixed order (PfSplit), or, with no workspace, are added into y
+// with fp32 atomics after a fill kernel clears y (a kernel, so that the
+// sequence can be captured in a graph; the order of those few additions
+// varies from run to run).
 template <typename F>
 static hipError_t launch_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
-                                 hipStream_t s) {
-  // 512-token tiles decode each weight half as often and feed more MFMAs per
-  // fragment read, but one takes about 1.7 times as long as a 256-token tile
-  // (measured): they are used when they fill at least two rounds of
-  // workgroups, or when 256-token tiles need more than one round and the
-  // 512-token rounds take fewer tile-times (1024 tokens x 14336 rows: one
-  // round of 224 tiles, against two rounds of 448)
-  const int64_t row_tiles = (n + kPfBN - 1) / kPfBN;
-  const int64_t tiles512 = row_tiles * ((t + 511) / 512), tiles256 = row_tiles * ((t + 255) / 256);
-  const bool use512 =
-      tiles512 >= 512 || (tiles256 > 256 && 17 * ((tiles512 + 255) / 256) < 10 * ((tiles256 + 255) / 256));
-  const int bt = use512 ? 512 : 256;
-  const int64_t tiles = row_tiles * ((t + bt - 1) / bt);
-  const int64_t steps = k / kPfKS;
-  int64_t split = 1;
-  if (tiles < 256) split = max(int64_t(1), 256 / tiles);  // fewer tiles than CUs
-  split = min(split, max(int64_t(1), steps / 8));
-  split = min(split, int64_t(16));
-  // a whole number of loop iterations per split (only the last split ends
-  // early): a step past the end skips its arithmetic but still waits for the
-  // loads in flight, and measured nearly as slow as a full one
-  const int64_t split_steps = ((steps + split - 1) / split + kPfUnroll - 1) / kPfUnroll * kPfUnroll;
-  split = (steps + split_steps - 1) / split_steps;
-  if (split > 1) {
+                                 void* ws, hipStream_t s) {
+  const PfPlan p = prefill_plan(t, n, k);
+  float* const part = static_cast<float*>(ws);
+  if (p.split > 1 && !part) {
     const int64_t count = t * n;
     hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)(count / 4096 + 1)), dim3(256), 0, s, y, count);
   }
-  // (the one-dimensional grid and the clear stay well inside 32-bit counts)
-  if (bt == 512 && split == 1 && tiles % 256 != 0 && tiles % 256 <= 64 && tiles < (int64_t(1) << 28) &&
-      n < (int64_t(1) << 24)) {
-    // the last round would be at most a quarter full: split its tiles over K
-    // so that it takes about 1 / tail_split of a round.  (A half-full last
-    // round is left alone: splitting it measured 2 % slower at 4096 tokens x
-    // 14336 rows, the clock of the power-limited chip being higher while
-    // half of it idles, and the clear and atomics costing extra.)
-    const int64_t tail = tiles % 256, n_full = tiles - tail;
-    int64_t tail_split = min(256 / tail, int64_t(4));
-    tail_split = min(tail_split, max(int64_t(1), steps / 12));
-    const int64_t tail_steps = ((steps + tail_split - 1) / tail_split + kPfUnroll - 1) / kPfUnroll * kPfUnroll;
-    tail_split = (steps + tail_steps - 1) / tail_steps;
-    if (tail_split > 1) {
-      const int64_t t_zero = n_full / row_tiles * 512;  // first token row of a split tile
+  if (p.split == 1 && p.tail_split > 1) {
+    if (!part) {
+      const int64_t t_zero = p.n_full / p.row_tiles * 512;  // first token row of a split tile
       const int64_t count = (t - t_zero) * n;
       hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)(count / 4096 + 1)), dim3(256), 0, s, y + t_zero * n,
                          count);
-      hipLaunchKernelGGL((prefill_tail_kernel<F>), dim3((unsigned)(n_full + tail * tail_split)),
-                         dim3(64 * kPfWaves), 0, s, (const uint8_t*)w, (const uint16_t*)x, y, (int)t, (int)n,
-                         (int)k, (int)row_tiles, (int)n_full, (int)tail_split, (int)tail_steps);
-      return hipGetLastError();
     }
+    hipLaunchKernelGGL((prefill_tail_kernel<F>), dim3((unsigned)(p.n_full + p.tail * p.tail_split)),
+                       dim3(64 * kPfWaves), 0, s, (const uint8_t*)w, (const uint16_t*)x, y, (int)t, (int)n, (int)k,
+                       (int)p.row_tiles, (int)p.n_full, (int)p.tail_split, (int)p.tail_steps, part);
+    if (part)
+      hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)(p.tail * 512 / 8)), dim3(256), 0, s, part, y, (int)t,
+                         (int)n, 512, (int)p.row_tiles, (int)p.n_full, (int)p.tail_split);
+    return hipGetLastError();
   }
-  const dim3 grid((unsigned)row_tiles, (unsigned)((t + bt - 1) / bt), (unsigned)split);
-  if (bt == 512)
+  const dim3 grid((unsigned)p.row_tiles, (unsigned)((t + p.bt - 1) / p.bt), (unsigned)p.split);
+  if (p.bt == 512)
     hipLaunchKernelGGL((prefill_kernel<F, 512>), grid, dim3(64 * kPfWaves), 0, s, (const uint8_t*)w,
-                       (const uint16_t*)x, y, (int)t, (int)n, (int)k, (int)split_steps);
+                       (const uint16_t*)x, y, (int)t, (int)n, (int)k, (int)p.split_steps, part);
   else
     hipLaunchKernelGGL((prefill_kernel<F, 256>), grid, dim3(64 * kPfWaves), 0, s, (const uint8_t*)w,
-                       (const uint16_t*)x, y, (int)t, (int)n, (int)k, (int)split_steps);
+                       (const uint16_t*)x, y, (int)t, (int)n, (int)k, (int)p.split_steps, part);
+  if (p.split > 1 && part)
+    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)(p.tiles * p.bt / 8)), dim3(256), 0, s, part, y, (int)t,
+                       (int)n, p.bt, (int)p.row_tiles, 0, (int)p.split);
   return hipGetLastError();
 }
 
-hipError_t launch_q4k_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s) {
-  return launch_prefill<Q4kPrefill>(w, x, y, t, n, k, s);
+hipError_t launch_q4k_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, void* ws,
+                              hipStream_t s) {
+  return launch_prefill<Q4kPrefill>(w, x, y, t, n, k, ws, s);
 }
-hipError_t launch_nvfp4_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k,
+hipError_t launch_nvfp4_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, void* ws,
                                 hipStream_t s) {
-  return launch_prefill<Nvfp4Prefill>(w, x, y, t, n, k, s);
+  return launch_prefill<Nvfp4Prefill>(w, x, y, t, n, k, ws, s);
 }
-hipError_t launch_tq1_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, hipStream_t s) {
-  return launch_prefill<Tq1Prefill>(w, x, y, t, n, k, s);
+hipError_t launch_tq1_prefill(const void* w, const void* x, float* y, int64_t t, int64_t n, int64_t k, void* ws,
+                              hipStream_t s) {
+  return launch_prefill<Tq1Prefill>(w, x, y, t, n, k, ws, s);
 }
 
 }  // namespace qgemv

@@ -34,9 +34,10 @@ GEMV_EX_SYMBOLS = ("qgemv_q4k_ex", "qgemv_nvfp4_ex", "qgemv_tq1_ex", "qgemv_f16_
 DEQUANT_SYMBOLS = ("qdequant_q4k", "qdequant_nvfp4", "qdequant_tq1")
 ROWS_SYMBOLS = ("qget_rows_q4k", "qget_rows_nvfp4", "qget_rows_tq1")
 GEMM_SYMBOLS = ("qgemm_q4k", "qgemm_nvfp4", "qgemm_tq1")
-ALL_SYMBOLS = GEMV_SYMBOLS + GEMV_EX_SYMBOLS + DEQUANT_SYMBOLS + ROWS_SYMBOLS + GEMM_SYMBOLS + (
-    "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror", "qgemv_last_hip_error",
-    "qgemv_build_id")
+GEMM_WS_SYMBOLS = ("qgemm_q4k_ws", "qgemm_nvfp4_ws", "qgemm_tq1_ws")
+ALL_SYMBOLS = GEMV_SYMBOLS + GEMV_EX_SYMBOLS + DEQUANT_SYMBOLS + ROWS_SYMBOLS + GEMM_SYMBOLS + GEMM_WS_SYMBOLS + (
+    "qgemm_workspace_bytes", "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror",
+    "qgemv_last_hip_error", "qgemv_build_id")
 
 
 class Epilogue(ctypes.Structure):
@@ -79,6 +80,12 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [P, P, P, I64, I64, I64, P]
+    for name in GEMM_WS_SYMBOLS:
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
+    lib.qgemm_workspace_bytes.restype = ctypes.c_int64
+    lib.qgemm_workspace_bytes.argtypes = [I64, I64, I64]
     lib.qgemv_read_ceiling.restype = ctypes.c_int
     lib.qgemv_read_ceiling.argtypes = [P, I64, P, P]
     lib.qgemv_read_sink_len.restype = ctypes.c_int64
@@ -299,6 +306,39 @@ def qgemm_tq1(w, x, y, T, M, K, stream=None):
     return y
 
 
+def qgemm_workspace_bytes(T, M, K) -> int:
+    """Bytes of workspace qgemm_*_ws needs for a T x M x K prefill (0: none)."""
+    n = _lib.qgemm_workspace_bytes(int(T), int(M), int(K))
+    if n < 0:
+        raise QgemvError(int(n), "qgemm_workspace_bytes")
+    return int(n)
+
+
+def _gemm_ws(name, w, x, y, T, M, K, ws, stream):
+    _gemm_sizes(name, w, x, y, T, M, K)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(getattr(_lib, name)(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K),
+                               None if ws is None else _addr(ws), nbytes, _stream(stream)), name)
+    return y
+
+
+def qgemm_q4k_ws(w, x, y, T, M, K, ws, stream=None):
+    """Prefill with a run-to-run identical result: K splits go through `ws`
+    (a device tensor of at least qgemm_workspace_bytes bytes; None when that
+    is 0)."""
+    return _gemm_ws("qgemm_q4k_ws", w, x, y, T, M, K, ws, stream)
+
+
+def qgemm_nvfp4_ws(w, x, y, T, M, K, ws, stream=None):
+    """NVFP4 prefill through a workspace (see qgemm_q4k_ws)."""
+    return _gemm_ws("qgemm_nvfp4_ws", w, x, y, T, M, K, ws, stream)
+
+
+def qgemm_tq1_ws(w, x, y, T, M, K, ws, stream=None):
+    """TQ1_0 prefill through a workspace (see qgemm_q4k_ws)."""
+    return _gemm_ws("qgemm_tq1_ws", w, x, y, T, M, K, ws, stream)
+
+
 def _dequant(name, w, out, M, K, stream):
     if M > 0 and K > 0:
         _need(w, weight_bytes(name.split("_")[1], M, K), "w", name)
@@ -344,6 +384,7 @@ GEMV_EX = {"q4k": qgemv_q4k_ex, "nvfp4": qgemv_nvfp4_ex, "tq1": qgemv_tq1_ex, "f
 DEQUANT = {"q4k": qdequant_q4k, "nvfp4": qdequant_nvfp4, "tq1": qdequant_tq1}
 GET_ROWS = {"q4k": qget_rows_q4k, "nvfp4": qget_rows_nvfp4, "tq1": qget_rows_tq1}
 GEMM = {"q4k": qgemm_q4k, "nvfp4": qgemm_nvfp4, "tq1": qgemm_tq1}
+GEMM_WS = {"q4k": qgemm_q4k_ws, "nvfp4": qgemm_nvfp4_ws, "tq1": qgemm_tq1_ws}
 
 
 def gemv(fmt: str, w, x, M: int, K: int, y=None, stream=None):

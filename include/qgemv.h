@@ -48,7 +48,8 @@ enum {
   QGEMV_E_ALIGN = -3, /* a pointer is not aligned as required */
   QGEMV_E_HIP = -4,   /* the HIP runtime rejected the launch */
   QGEMV_E_ALIAS = -5, /* the output overlaps an input */
-  QGEMV_E_DTYPE = -6  /* an element-type code is not one of QGEMV_F32 / QGEMV_F16 / QGEMV_BF16 */
+  QGEMV_E_DTYPE = -6, /* an element-type code is not one of QGEMV_F32 / QGEMV_F16 / QGEMV_BF16 */
+  QGEMV_E_WORKSPACE = -7 /* a workspace smaller than qgemm_workspace_bytes asks for */
 };
 
 /* Element types of epilogue vectors and materialised rows: fp32, IEEE binary16
@@ -169,6 +170,24 @@ int qgemm_nvfp4(const void* w, const void* x_bf16, float* y, int64_t T, int64_t 
  * unpacked into a tile that the matrix unit reads). */
 int qgemm_tq1(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
               struct ihipStream_t* stream);
+
+/* Prefill whose result does not vary from run to run: the same as qgemm_* but
+ * the partial sums of tiles split over K go to `workspace` (device memory
+ * owned by the caller) and a second kernel on the same stream adds them in a
+ * fixed order into y, so no atomics and no clearing of y are involved.
+ * qgemm_workspace_bytes(T, M, K) gives the bytes needed (0 when no tile is
+ * split: the workspace may then be NULL; QGEMV_E_SHAPE for sizes no qgemm_*
+ * call accepts).  The workspace must be 256-byte aligned, at least that large
+ * and overlap none of W, x and y; its contents need no initialisation and
+ * are overwritten, so calls that overlap in time must not share it.  Errors:
+ * as qgemm_*, plus QGEMV_E_WORKSPACE when workspace_bytes is too small. */
+int64_t qgemm_workspace_bytes(int64_t T, int64_t M, int64_t K);
+int qgemm_q4k_ws(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K, void* workspace,
+                 int64_t workspace_bytes, struct ihipStream_t* stream);
+int qgemm_nvfp4_ws(const void* w, const void* x_bf16, float* y, int64_t T, int64_t M, int64_t K, void* workspace,
+                   int64_t workspace_bytes, struct ihipStream_t* stream);
+int qgemm_tq1_ws(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K, void* workspace,
+                 int64_t workspace_bytes, struct ihipStream_t* stream);
 
 /* fp32 materialisation out[M][K] of the same formats (same W conventions as
  * above; the same as qget_rows_* with rows = NULL, nrows = M, QGEMV_F32).  Each value is the correctly rounded fp32 of the exact weight, which

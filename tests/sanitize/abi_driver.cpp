@@ -14,6 +14,7 @@
 
 extern "C" int g_stub_calls;
 extern "C" int g_stub_status;
+extern "C" void* g_stub_ws;
 
 static int g_fail = 0;
 
@@ -170,6 +171,40 @@ int main() {
     EXPECT(gemms[i](w, x, (float*)x, 7, 5, 512, nullptr), QGEMV_E_ALIAS, 0);
   }
   EXPECT(qgemm_nvfp4(w, x, (float*)out, 7, 5, 96, nullptr), QGEMV_E_SHAPE, 0);  // K % 64
+
+  // prefill with a workspace: no K split at 7 x 5 x 512 (no workspace needed),
+  // 130 tokens x 4096 rows x K 4096 splits each of its 32 tiles 6 ways (8
+  // asked for, 64 steps rounded to whole 6-step iterations: 12 steps per
+  // split; 6 x 32 partial tiles of 256 x 128 fp32); pointer values far apart
+  // stand in for device memory
+  if (qgemm_workspace_bytes(7, 5, 512) != 0 || qgemm_workspace_bytes(0, 5, 512) != 0 ||
+      qgemm_workspace_bytes(130, 4096, 4096) != int64_t(32) * 6 * 256 * 128 * 4 ||
+      qgemm_workspace_bytes(-1, 5, 512) != QGEMV_E_SHAPE || qgemm_workspace_bytes(7, 5, 0) != QGEMV_E_SHAPE)
+    g_fail = 1;
+  typedef int (*gemm_ws_fn)(const void*, const void*, float*, int64_t, int64_t, int64_t, void*, int64_t,
+                            struct ihipStream_t*);
+  const gemm_ws_fn gemm_wss[] = {qgemm_q4k_ws, qgemm_nvfp4_ws, qgemm_tq1_ws};
+  const int64_t need = qgemm_workspace_bytes(130, 4096, 4096);
+  const void* bw = (const void*)(uintptr_t(1) << 40);
+  const void* bx = (const void*)(uintptr_t(2) << 40);
+  float* by = (float*)(uintptr_t(3) << 40);
+  void* bws = (void*)(uintptr_t(4) << 40);
+  for (int i = 0; i < 3; ++i) {
+    g_stub_ws = bws;
+    EXPECT(gemm_wss[i](w, x, (float*)out, 7, 5, 512, nullptr, 0, nullptr), QGEMV_OK, 1);
+    if (g_stub_ws != nullptr) g_fail = 1;  // nothing split: no workspace handed on
+    EXPECT(gemm_wss[i](bw, bx, by, 130, 4096, 4096, bws, need, nullptr), QGEMV_OK, 1);
+    if (g_stub_ws != bws) g_fail = 1;
+    EXPECT(gemm_wss[i](bw, bx, by, 130, 4096, 4096, nullptr, need, nullptr), QGEMV_E_NULL, 0);
+    EXPECT(gemm_wss[i](bw, bx, by, 130, 4096, 4096, (char*)bws + 16, need, nullptr), QGEMV_E_ALIGN, 0);
+    EXPECT(gemm_wss[i](bw, bx, by, 130, 4096, 4096, bws, need - 1, nullptr), QGEMV_E_WORKSPACE, 0);
+    EXPECT(gemm_wss[i](bw, bx, by, 130, 4096, 4096, (void*)((char*)by + 256), need, nullptr), QGEMV_E_ALIAS, 0);
+    EXPECT(gemm_wss[i](bw, bx, by, 130, 4096, 4096, (void*)((char*)bw - 256), need, nullptr), QGEMV_E_ALIAS, 0);
+    EXPECT(gemm_wss[i](bw, bx, by, 0, 4096, 4096, nullptr, 0, nullptr), QGEMV_OK, 0);
+  }
+  g_stub_ws = bws;
+  EXPECT(qgemm_q4k(bw, bx, by, 130, 4096, 4096, nullptr), QGEMV_OK, 1);
+  if (g_stub_ws != nullptr) g_fail = 1;  // the plain call splits with atomics
 
   // read probe, strings
   EXPECT(qgemv_read_ceiling(w, 65536, (float*)out, nullptr), QGEMV_OK, 1);

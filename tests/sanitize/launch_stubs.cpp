@@ -5,8 +5,10 @@
 
 extern "C" int g_stub_calls;
 extern "C" int g_stub_status;
+extern "C" void* g_stub_ws;  // the workspace the last prefill launcher was given
 int g_stub_calls = 0;
 int g_stub_status = 0;
+void* g_stub_ws = nullptr;
 
 namespace qgemv {
 
@@ -36,11 +38,18 @@ hipError_t launch_nvfp4_get_rows(const void*, int64_t, int64_t, const int32_t*, 
 hipError_t launch_tq1_get_rows(const void*, int64_t, int64_t, const int32_t*, int64_t, void*, int, hipStream_t) {
   return reached();
 }
-hipError_t launch_q4k_prefill(const void*, const void*, float*, int64_t, int64_t, int64_t, hipStream_t) { return reached(); }
-hipError_t launch_nvfp4_prefill(const void*, const void*, float*, int64_t, int64_t, int64_t, hipStream_t) {
+hipError_t launch_q4k_prefill(const void*, const void*, float*, int64_t, int64_t, int64_t, void* ws, hipStream_t) {
+  g_stub_ws = ws;
   return reached();
 }
-hipError_t launch_tq1_prefill(const void*, const void*, float*, int64_t, int64_t, int64_t, hipStream_t) { return reached(); }
+hipError_t launch_nvfp4_prefill(const void*, const void*, float*, int64_t, int64_t, int64_t, void* ws, hipStream_t) {
+  g_stub_ws = ws;
+  return reached();
+}
+hipError_t launch_tq1_prefill(const void*, const void*, float*, int64_t, int64_t, int64_t, void* ws, hipStream_t) {
+  g_stub_ws = ws;
+  return reached();
+}
 hipError_t launch_read_ceiling(const void*, int64_t, float*, hipStream_t) { return reached(); }
 int64_t read_sink_len(int64_t bytes) { return (bytes + 32767) / 32768; }
 

@@ -25,7 +25,7 @@ def q():
 
 def test_header_symbols_exported(q):
     names = _header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 28, names
     lib = q.lib()
     for n in names:
         assert hasattr(lib, n), n

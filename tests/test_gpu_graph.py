@@ -133,3 +133,29 @@ def test_prefill_graph_replays(q, fmt, t, m, k):
         assert not np.isnan(got).any()
         g_ = got[np.ix_(toks, rows)]
         assert np.all(np.abs(g_ - yr) <= 1e-3 * ar + 1e-5), (fmt, t, m, k, r)
+
+
+@pytest.mark.parametrize("fmt,t,m,k", [
+    ("q4k", 130, 4096, 4096),      # every tile split: partials, then the reduction kernel
+    ("tq1", 1025, 21888, 2048),    # the last round split
+])
+def test_prefill_ws_graph_replays(q, fmt, t, m, k):
+    # the workspace path in a graph: every replay bit-identical to the eager
+    # call, with y and the workspace overwritten between replays
+    w = synth.weights(fmt, m, k, synth.W_SEED + 331)
+    x = np.stack([synth.activations(fmt, k, synth.X_SEED + 331 + i) for i in range(t)])
+    wd, xd = _dev(w), _dev(x.view(np.int16))
+    nws = q.qgemm_workspace_bytes(t, m, k)
+    assert nws > 0
+    ws = torch.empty(nws // 4, dtype=torch.float32, device=DEV)
+    y = torch.full((t, m), float("nan"), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    g = _capture(lambda h: q.GEMM_WS[fmt](wd, xd, y, t, m, k, ws, h), s)
+    want = y.clone()
+    assert not torch.isnan(want).any()
+    for r in range(REPLAYS):
+        def disturb():
+            y.fill_(1000.0 * (r + 1))
+            ws.fill_(-7.0)
+        _replay(g, s, disturb)
+        assert torch.equal(y.view(torch.int32), want.view(torch.int32)), (fmt, r)
