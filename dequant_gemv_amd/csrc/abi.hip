@@ -132,9 +132,12 @@ int get_rows(Fmt f, const void* w, int64_t m, int64_t k, const int32_t* rows, in
   }
 }
 
-// use_ws: the _ws entry points (K splits through the caller's workspace);
-// otherwise K splits add into y with atomics.
-int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, int64_t k, bool use_ws, void* ws,
+// Where the partial sums of tiles split over K go: added into y with atomics
+// (qgemm_*), a caller's workspace (qgemm_*_ws) or the library's own array
+// (qgemm_q4k_noalloc).
+enum Split { kAtomics, kCallerWs, kScratchWs };
+
+int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, int64_t k, Split mode, void* ws,
          int64_t ws_bytes, hipStream_t s) {
   int rc = check_shape(f, m, k);
   if (rc != QGEMV_OK) return rc;
@@ -148,15 +151,17 @@ int gemm(Fmt f, const void* w, const void* x, float* y, int64_t t, int64_t m, in
   const int64_t yb = t * m * 4, wb = weight_bytes(f, m, k), xb = t * k * 2;
   if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return QGEMV_E_ALIAS;
   void* wsp = nullptr;
-  if (use_ws) {
-    const int64_t need = qgemv::prefill_workspace_bytes(t, m, k);
-    if (need > 0) {
-      if (!ws) return QGEMV_E_NULL;
-      if (misaligned(ws, 256)) return QGEMV_E_ALIGN;
-      if (ws_bytes < need) return QGEMV_E_WORKSPACE;
-      if (overlap(ws, need, y, yb) || overlap(ws, need, w, wb) || overlap(ws, need, x, xb)) return QGEMV_E_ALIAS;
-      wsp = ws;
-    }
+  const int64_t need = mode == kAtomics ? 0 : qgemv::prefill_workspace_bytes(t, m, k);
+  if (need > 0 && mode == kCallerWs) {
+    if (!ws) return QGEMV_E_NULL;
+    if (misaligned(ws, 256)) return QGEMV_E_ALIGN;
+    if (ws_bytes < need) return QGEMV_E_WORKSPACE;
+    if (overlap(ws, need, y, yb) || overlap(ws, need, w, wb) || overlap(ws, need, x, xb)) return QGEMV_E_ALIAS;
+    wsp = ws;
+  } else if (need > 0) {
+    if (need > qgemv::kScratchBytes) return QGEMV_E_WORKSPACE;
+    const hipError_t e = qgemv::scratch_address(s, &wsp);
+    if (e != hipSuccess) return finish(e);
   }
   switch (f) {
     case kQ4k: return finish(qgemv::launch_q4k_prefill(w, x, y, t, m, k, wsp, s));
@@ -237,13 +242,13 @@ int qget_rows_tq1(const void* w, int64_t M, int64_t K, const int32_t* rows, int6
 }
 
 int qgemm_q4k(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
-  return gemm(kQ4k, w, x, y, T, M, K, false, nullptr, 0, s);
+  return gemm(kQ4k, w, x, y, T, M, K, kAtomics, nullptr, 0, s);
 }
 int qgemm_nvfp4(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
-  return gemm(kNvfp4, w, x, y, T, M, K, false, nullptr, 0, s);
+  return gemm(kNvfp4, w, x, y, T, M, K, kAtomics, nullptr, 0, s);
 }
 int qgemm_tq1(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, struct ihipStream_t* s) {
-  return gemm(kTq1, w, x, y, T, M, K, false, nullptr, 0, s);
+  return gemm(kTq1, w, x, y, T, M, K, kAtomics, nullptr, 0, s);
 }
 
 int64_t qgemm_workspace_bytes(int64_t T, int64_t M, int64_t K) {
@@ -253,15 +258,20 @@ int64_t qgemm_workspace_bytes(int64_t T, int64_t M, int64_t K) {
 }
 int qgemm_q4k_ws(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, void* ws, int64_t ws_bytes,
                  struct ihipStream_t* s) {
-  return gemm(kQ4k, w, x, y, T, M, K, true, ws, ws_bytes, s);
+  return gemm(kQ4k, w, x, y, T, M, K, kCallerWs, ws, ws_bytes, s);
 }
 int qgemm_nvfp4_ws(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, void* ws,
                    int64_t ws_bytes, struct ihipStream_t* s) {
-  return gemm(kNvfp4, w, x, y, T, M, K, true, ws, ws_bytes, s);
+  return gemm(kNvfp4, w, x, y, T, M, K, kCallerWs, ws, ws_bytes, s);
 }
 int qgemm_tq1_ws(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K, void* ws, int64_t ws_bytes,
                  struct ihipStream_t* s) {
-  return gemm(kTq1, w, x, y, T, M, K, true, ws, ws_bytes, s);
+  return gemm(kTq1, w, x, y, T, M, K, kCallerWs, ws, ws_bytes, s);
+}
+
+int qgemm_q4k_noalloc(const void* w, const void* x, float* y, int64_t T, int64_t M, int64_t K,
+                      struct ihipStream_t* s) {
+  return gemm(kQ4k, w, x, y, T, M, K, kScratchWs, nullptr, 0, s);
 }
 
 int64_t qgemv_read_sink_len(int64_t bytes) { return bytes > 0 ? qgemv::read_sink_len(bytes) : 0; }

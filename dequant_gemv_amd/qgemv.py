@@ -21,6 +21,7 @@ QGEMV_E_ALIGN = -3
 QGEMV_E_HIP = -4
 QGEMV_E_ALIAS = -5
 QGEMV_E_DTYPE = -6
+QGEMV_E_WORKSPACE = -7
 
 # element type codes
 QGEMV_F32 = 0
@@ -36,7 +37,7 @@ ROWS_SYMBOLS = ("qget_rows_q4k", "qget_rows_nvfp4", "qget_rows_tq1")
 GEMM_SYMBOLS = ("qgemm_q4k", "qgemm_nvfp4", "qgemm_tq1")
 GEMM_WS_SYMBOLS = ("qgemm_q4k_ws", "qgemm_nvfp4_ws", "qgemm_tq1_ws")
 ALL_SYMBOLS = GEMV_SYMBOLS + GEMV_EX_SYMBOLS + DEQUANT_SYMBOLS + ROWS_SYMBOLS + GEMM_SYMBOLS + GEMM_WS_SYMBOLS + (
-    "qgemm_workspace_bytes", "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror",
+    "qgemm_q4k_noalloc", "qgemm_workspace_bytes", "qgemv_read_ceiling", "qgemv_read_sink_len", "qgemv_strerror",
     "qgemv_last_hip_error", "qgemv_build_id")
 
 
@@ -84,6 +85,8 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
+    lib.qgemm_q4k_noalloc.restype = ctypes.c_int
+    lib.qgemm_q4k_noalloc.argtypes = [P, P, P, I64, I64, I64, P]
     lib.qgemm_workspace_bytes.restype = ctypes.c_int64
     lib.qgemm_workspace_bytes.argtypes = [I64, I64, I64]
     lib.qgemv_read_ceiling.restype = ctypes.c_int
@@ -327,6 +330,20 @@ def qgemm_q4k_ws(w, x, y, T, M, K, ws, stream=None):
     (a device tensor of at least qgemm_workspace_bytes bytes; None when that
     is 0)."""
     return _gemm_ws("qgemm_q4k_ws", w, x, y, T, M, K, ws, stream)
+
+
+# Size of the library's own workspace array behind qgemm_q4k_noalloc.
+NOALLOC_MAX_BYTES = 32 << 20
+
+
+def qgemm_q4k_noalloc(w, x, y, T, M, K, stream=None):
+    """qgemm_q4k_ws without a caller workspace: the K splits go through a fixed
+    32 MiB array per device inside the library, so the call allocates nothing.
+    Calls on one device that overlap in time share that array and race."""
+    _gemm_sizes("qgemm_q4k_noalloc", w, x, y, T, M, K)
+    _check(_lib.qgemm_q4k_noalloc(_addr(w), _addr(x), _addr(y), int(T), int(M), int(K), _stream(stream)),
+           "qgemm_q4k_noalloc")
+    return y
 
 
 def qgemm_nvfp4_ws(w, x, y, T, M, K, ws, stream=None):

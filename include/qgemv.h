@@ -189,6 +189,24 @@ int qgemm_nvfp4_ws(const void* w, const void* x_bf16, float* y, int64_t T, int64
 int qgemm_tq1_ws(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K, void* workspace,
                  int64_t workspace_bytes, struct ihipStream_t* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): Q4_K
+ * prefill with the same result as qgemm_q4k_ws, whose workspace is instead a
+ * fixed device array inside the library, QGEMV_NOALLOC_MAX_BYTES (32 MiB)
+ * per device, reserved on each device the library is used on until the
+ * process ends.  The call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine.  Its first call on a device looks the array's
+ * address up once (thread-safe).  The caller passes W, x and y as for
+ * qgemm_q4k.  Errors: as qgemm_q4k, plus QGEMV_E_WORKSPACE when
+ * qgemm_workspace_bytes(T, M, K) exceeds QGEMV_NOALLOC_MAX_BYTES.  Nothing in
+ * the array needs to start at zero; every call on one device shares that
+ * device's array and leaves its own partial sums there, so calls on one device
+ * that overlap in time (on different streams, or from different threads)
+ * race and must be serialised by the caller. */
+#define QGEMV_NOALLOC_MAX_BYTES (32ll << 20)
+int qgemm_q4k_noalloc(const void* w, const void* x_f16, float* y, int64_t T, int64_t M, int64_t K,
+                      struct ihipStream_t* stream);
+
 /* fp32 materialisation out[M][K] of the same formats (same W conventions as
  * above; the same as qget_rows_* with rows = NULL, nrows = M, QGEMV_F32).  Each value is the correctly rounded fp32 of the exact weight, which
  * for these formats is the exact weight itself whenever it is representable

@@ -15,6 +15,7 @@
 extern "C" int g_stub_calls;
 extern "C" int g_stub_status;
 extern "C" void* g_stub_ws;
+extern "C" void* const g_stub_scratch;
 
 static int g_fail = 0;
 
@@ -205,6 +206,22 @@ int main() {
   g_stub_ws = bws;
   EXPECT(qgemm_q4k(bw, bx, by, 130, 4096, 4096, nullptr), QGEMV_OK, 1);
   if (g_stub_ws != nullptr) g_fail = 1;  // the plain call splits with atomics
+
+  // prefill through the library's own 32 MiB array: the argument checks come
+  // first; a split needing more than the array is refused before any HIP call
+  // (4608 x 8192 x 4096 asks for 64 MiB); an unsplit call needs no array
+  EXPECT(qgemm_q4k_noalloc(bw, bx, by, 4608, 8192, 4096, nullptr), QGEMV_E_WORKSPACE, 0);
+  EXPECT(qgemm_q4k_noalloc(bw, bx, by, 130, 4096, 4000, nullptr), QGEMV_E_SHAPE, 0);
+  EXPECT(qgemm_q4k_noalloc(bw, bx, by, -1, 4096, 4096, nullptr), QGEMV_E_SHAPE, 0);
+  EXPECT(qgemm_q4k_noalloc(nullptr, bx, by, 130, 4096, 4096, nullptr), QGEMV_E_NULL, 0);
+  EXPECT(qgemm_q4k_noalloc(bw, bx, (float*)((char*)by + 2), 130, 4096, 4096, nullptr), QGEMV_E_ALIGN, 0);
+  EXPECT(qgemm_q4k_noalloc(bw, bx, (float*)bx, 130, 4096, 4096, nullptr), QGEMV_E_ALIAS, 0);
+  EXPECT(qgemm_q4k_noalloc(bw, bx, by, 0, 4096, 4096, nullptr), QGEMV_OK, 0);
+  g_stub_ws = bws;
+  EXPECT(qgemm_q4k_noalloc(w, x, (float*)out, 7, 5, 512, nullptr), QGEMV_OK, 1);
+  if (g_stub_ws != nullptr) g_fail = 1;
+  EXPECT(qgemm_q4k_noalloc(bw, bx, by, 130, 4096, 4096, nullptr), QGEMV_OK, 1);
+  if (g_stub_ws != g_stub_scratch) g_fail = 1;  // the split goes through the array
 
   // read probe, strings
   EXPECT(qgemv_read_ceiling(w, 65536, (float*)out, nullptr), QGEMV_OK, 1);

@@ -9,6 +9,8 @@ extern "C" void* g_stub_ws;  // the workspace the last prefill launcher was give
 int g_stub_calls = 0;
 int g_stub_status = 0;
 void* g_stub_ws = nullptr;
+extern "C" void* const g_stub_scratch;
+void* const g_stub_scratch = (void*)(uintptr_t(5) << 40);
 
 namespace qgemv {
 
@@ -52,5 +54,10 @@ hipError_t launch_tq1_prefill(const void*, const void*, float*, int64_t, int64_t
 }
 hipError_t launch_read_ceiling(const void*, int64_t, float*, hipStream_t) { return reached(); }
 int64_t read_sink_len(int64_t bytes) { return (bytes + 32767) / 32768; }
+// stands in for the library's device array: a fixed fake address
+hipError_t scratch_address(hipStream_t, void** ptr) {
+  *ptr = g_stub_scratch;
+  return hipSuccess;
+}
 
 }  // namespace qgemv

@@ -25,7 +25,7 @@ def q():
 
 def test_header_symbols_exported(q):
     names = _header_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     lib = q.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -97,6 +97,23 @@ def test_gemm_validation(q, name, kmul):
     assert f(W, X, Y + 2, 3, 4, kmul, None) == q.QGEMV_E_ALIGN
     assert f(W, X, W + 16, 3, 4, kmul, None) == q.QGEMV_E_ALIAS
     assert f(W, X, X + 4, 3, 4, kmul, None) == q.QGEMV_E_ALIAS
+
+
+def test_gemm_noalloc_validation(q):
+    """The argument checks of qgemm_q4k_noalloc all come before it touches its
+    device array; a split needing more than the array is refused up front."""
+    f = q.lib().qgemm_q4k_noalloc
+    W, X, Y = A, A + (1 << 36), A + (2 << 36)
+    assert q.qgemm_workspace_bytes(4608, 8192, 4096) > q.NOALLOC_MAX_BYTES
+    assert q.qgemm_workspace_bytes(512, 4096, 14336) <= q.NOALLOC_MAX_BYTES
+    assert f(W, X, Y, 4608, 8192, 4096, None) == q.QGEMV_E_WORKSPACE
+    assert f(W, X, Y, 3, 4, 384, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 65535 * 128 + 1, 4, 256, None) == q.QGEMV_E_SHAPE
+    assert f(W, X, Y, 0, 4, 256, None) == q.QGEMV_OK
+    assert f(W, X, Y, 3, 0, 256, None) == q.QGEMV_OK
+    assert f(None, X, Y, 130, 4096, 4096, None) == q.QGEMV_E_NULL
+    assert f(W, X, Y + 2, 130, 4096, 4096, None) == q.QGEMV_E_ALIGN
+    assert f(W, X, X + 4, 130, 4096, 4096, None) == q.QGEMV_E_ALIAS
 
 
 @pytest.mark.parametrize("name,kmul,kmax", GEMVS)
