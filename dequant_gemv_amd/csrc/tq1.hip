@@ -35,10 +35,11 @@
 //
 // Digits from a table (the row-streaming kernel for K = 4096 and more than
 // 1024 rows): a 256-entry LDS table gives the five values digit_k(b) - 1 of a
-// byte as fp16 pairs, so a byte's five weights cost one 16-byte LDS read and
-// three v_dot2 instead of the arithmetic above (about 1 VALU instruction per
-// weight instead of 2; the table is built per workgroup, 16 copies side by
-// side so the lanes of a read never contend for a bank).
+// byte as fp16 pairs, so a byte's five weights cost one 16-byte LDS read,
+// one v_perm_b32 (the table address) and three v_dot2 instead of the
+// arithmetic above (about 0.85 VALU instructions per weight instead of 2;
+// the table is built per workgroup, 16 copies side by side so the lanes of a
+// read never contend for a bank), and each lane takes a quarter block.
 #include "device.hpp"
 #include "launch.hpp"
 #include "rows.hpp"
@@ -338,52 +339,55 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_rows_kernel(const uint8_t* __
   store_rows<R>(acc, out, pre, row0, nrows, 1.f, lane);
 }
 
-// Table-driven row-streaming variant (K = 4096, more than 1024 rows): the
-// same run and lanes as the row-streaming kernel above, the stage a ring of
-// eight one-KiB slots per wave (the lookahead never reaches further), and the
-// digits come from a table instead of arithmetic: entry b
-// (0..255) of the workgroup's digit table holds the fp16 values digit_k(b) - 1
-// (-1, 0 or +1, exact) as the pairs (k0, k1), (k2, k3), (k4, 0) and a zero
-// dword, so one 16-byte LDS read and three v_dot2_f32_f16 against the lane's
-// activation pairs (x[e0], x[e1]), (x[e2], x[e3]), (x[e4], 0) (e_k the element
-// digit k of the byte feeds) take a byte's five weights, and sum x (t - 1)
-// needs no correction term.  The table holds LREP copies of each entry side
-// by side and lane l reads copy l % LREP: for LREP = 16, any 16 consecutive
-// lanes read 16 different 16-byte bank groups whatever their bytes are.  Its
-// address is the byte itself moved to bit 8 (or 7) with the lane's copy offset
-// below, one v_perm_b32.
-// The activation pairs of a byte (three per byte, zero for a digit that feeds
-// nothing: digit 4 of qh bytes, the d bytes, lanes past the payload, blocks
-// past a short segment) are read once per segment position from the
-// workgroup's LDS copy of x and reused for all R rows; the two d values a lane
-// needs are read from the stage.  A lane's 16 bytes touch at most two blocks
-// (a block boundary falls between byte pairs): the running sum is taken at the
-// boundary and each part is scaled by its block's d.
+// Table-driven row-streaming kernel (K = 4096, more than 1024 rows).  The
+// digits come from a 256-entry table instead of arithmetic: entry b holds the
+// fp16 values digit_k(b) - 1 (-1, 0 or +1, exact) as the pairs (k0, k1), (k2,
+// k3), (k4, 0) and a zero dword, so one 16-byte LDS read and three
+// v_dot2_f32_f16 against the activation pairs (x[e0], x[e1]), (x[e2], x[e3]),
+// (x[e4], 0) (e_k the element digit k of the byte feeds) take a byte's five
+// weights, and the sum of x (t - 1) needs no correction term.  The table is
+// built per workgroup with LREP copies of each entry side by side and lane l
+// reads copy l % LREP: for LREP = 16 any 16 consecutive lanes read 16
+// different 16-byte bank groups whatever their bytes are.  The address is the
+// byte moved to bit 8 over the lane's copy offset, one v_perm_b32.
+//
+// A wave streams its R rows through a ring of eight one-KiB LDS slots (the
+// lookahead never reaches further), one 864-byte segment of 16 blocks per
+// unit.  Lane l takes the 13 payload bytes 13 q .. 13 q + 12 (q = l % 4) of
+// block l / 4 of the segment, so the 64 lanes cover the 16 blocks' 832
+// payload bytes exactly, a lane's bytes all belong to one block (one d per
+// unit) and no lane idles.  A lane's bytes start at segment offset
+// 54 (l / 4) + 13 q, which is 4-byte but not 16-byte aligned: the lane reads
+// the 16 bytes from the dword at or below it and byte-aligns them in
+// registers (v_alignbyte_b32 by the lane's misalignment); the last byte's
+// address takes one v_perm_b32 with a per-lane selector.  Per unit a lane
+// reads 13 table entries and issues 39 v_dot2_f32_f16 in one chain
+// (dependent v_dot2 issue back to back: more chains only cost the adds).
+// The activation pairs of a lane's 13 bytes are built once per workgroup from
+// its LDS copy of x and held in registers for all R rows.
 #ifndef QGEMV_TQ1_RING
 #define QGEMV_TQ1_RING 8  // stage slots (one KiB each) per wave of the table-driven kernel
 #endif
 constexpr int kTq1Ring = QGEMV_TQ1_RING;
-#ifndef QGEMV_TQ1_PIPE
-#define QGEMV_TQ1_PIPE 1  // read a unit's table entries one unit ahead of its sums
-#endif
 
 template <int KS, int R, int W, int LREP>
-struct Tq1LutRows {
+struct Tq1TableRows {
   using S = StreamSchedule<kTq1SegBytes, R * KS, QGEMV_TQ1_AHEAD, QGEMV_TQ1_AHEAD, QGEMV_TQ1_FIRST, kTq1Ring>;
   static constexpr int kLutBytes = 256 * 16 * LREP;  // at LDS offset 0
   static constexpr int kXBytes = KS * 8192;
-  static constexpr int kPairBytes = KS * 16 * 64 * 16;  // three activation pairs per (byte, lane) of a segment
-  static constexpr int kSlots = KS * 1024 / (64 * W);   // pair entries built per thread
+  static constexpr int kEntries = 13 * 64;  // activation pair entries (byte, lane) per segment
+  static constexpr int kPairBytes = KS * kEntries * 16;
+  static constexpr int kSlots = (KS * kEntries + 64 * W - 1) / (64 * W);  // entries built per thread
   static constexpr int kLds = kLutBytes + W * S::kStage + kXBytes + 16 + kPairBytes;  // + a zero element
   static_assert(LREP == 8 || LREP == 16, "table copies");
   static_assert(W == 4 || W == 8, "waves per workgroup");
 };
 
-// LDS bytes of a row-streaming TQ1_0 launch (what the launcher checks
-// against the 160 KiB of a workgroup).
-constexpr int tq1_lut_lds(int ks, int r, int w, int lrep) {
+// LDS bytes of a table-driven launch (what the launcher checks against the
+// 160 KiB of a workgroup).
+constexpr int tq1_table_lds(int ks, int r, int w, int lrep) {
   const int loads = (r * ks * kTq1SegBytes + 1023) / 1024;
-  return 256 * 16 * lrep + w * (loads < kTq1Ring ? loads : kTq1Ring) * 1024 + ks * 8192 + 16 + ks * 16 * 64 * 16;
+  return 256 * 16 * lrep + w * (loads < kTq1Ring ? loads : kTq1Ring) * 1024 + ks * 8192 + 16 + ks * 13 * 64 * 16;
 }
 
 // fp16 bits of digit_k(b) - 1 for k = 0..4 (same recurrence as tq1_digits on
@@ -400,15 +404,12 @@ __device__ __forceinline__ void tq1_lut_codes(unsigned b, unsigned (&h)[5]) {
 }
 
 template <int KS, int R, int W, int LREP, typename Out>
-__global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __restrict__ w,
-                                                              const uint16_t* __restrict__ x,
-                                                              Out out, int n, int nb) {
-  using C = Tq1LutRows<KS, R, W, LREP>;
+__global__ __launch_bounds__(64 * W) void tq1_gemv_table_kernel(const uint8_t* __restrict__ w,
+                                                                const uint16_t* __restrict__ x,
+                                                                Out out, int n, int nb) {
+  using C = Tq1TableRows<KS, R, W, LREP>;
   using S = typename C::S;
-  // rows of KS full segments (nb == 16 KS, checked by the launcher): the
-  // run's unit offsets are compile-time constants
-  constexpr int kRowBytes = KS * kTq1SegBytes;
-  constexpr int nbs_last = kTq1SegBlocks;
+  constexpr int kRowBytes = KS * kTq1SegBytes;  // nb == 16 KS, checked by the launcher
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
   unsigned char* const lut = lds;
   unsigned char* const xs = lds + C::kLutBytes + W * S::kStage;  // x, then a zero element
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
   stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
 
   // The digit table: thread t computes entry b = t % 256 and writes H = 64W /
-  // 256 ... copies of it; copy (b + H j + t / 256) % LREP on step j, so the
+  // 256 ... of its copies, copy (b + H j + t / 256) % LREP on step j, so the
   // 16 consecutive entries written by 16 consecutive lanes land in 16
   // different bank groups.
   {
@@ -443,52 +444,43 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
   }
   if (threadIdx.x == 0) *reinterpret_cast<unsigned*>(xs + C::kXBytes) = 0u;
 
-  // Activation pairs of every (byte i, lane l) of a segment, built once by
-  // the workgroup after the copy of x lands: digit k of payload byte pos
-  // feeds element base + k * stride of its block (qs[0..31]: pos, 32;
-  // qs[32..47]: pos + 128, 16; qh: pos + 192, 4 with no fifth digit); the d
-  // bytes, lanes past the payload and blocks past a short last segment read
-  // the zero element.  Entry (i, l) of segment sg (16 bytes: (x[e0], x[e1]),
-  // (x[e2], x[e3]), (x[e4], 0), 0) sits at [sg][i][l], so the lanes of one
-  // read take consecutive 16-byte slots (no bank conflict).  Addresses first,
-  // then every read, then the writes.
+  // Activation pairs of entry (byte i, lane l) of segment sg: lane l's byte
+  // i is payload byte pos = 13 (l % 4) + i of block l / 4, whose digit k
+  // feeds element base + k * stride of the block (qs[0..31]: pos, 32;
+  // qs[32..47]: pos + 128, 16; qh: pos + 192, 4 with no fifth digit, which
+  // reads the zero element).  The entry sits in slot (sg * 13 + i) * 64 +
+  // (l ^ 4 i): a lane's reads of its 13 entries stay conflict-free, and the
+  // builders (thread t makes the entry of payload byte t % 52 of block t /
+  // 52, so the 64 lanes of a build step read about 64 different x words)
+  // write 16 different 16-byte bank groups per 16 lanes.
   uint32_t xoff[C::kSlots][5];
+  uint32_t slot[C::kSlots];
 #pragma unroll
   for (int j = 0; j < C::kSlots; ++j) {
     const int t = (int)threadIdx.x + j * 64 * W;
-    const int l = t & 63, i = (t >> 6) & 15, sg = t >> 10;
-    const int q = 16 * l + i;
-    const int blk = q / kTq1Bytes, pos = q - blk * kTq1Bytes;
-    const bool payload = l < 54 && pos < 52 && blk < (sg == KS - 1 ? nbs_last : kTq1SegBlocks);
+    const int bg = t / 52, pos = t - 52 * bg;
+    const int sg = bg >> 4, blk = bg & 15;
+    const int q = pos / 13, i = pos - 13 * q;
+    slot[j] = (uint32_t)(((sg * 13 + i) * 64 + ((blk * 4 + q) ^ (4 * i))) * 16);
+    const bool valid = t < KS * C::kEntries;
     const int base = pos < 32 ? pos : pos < 48 ? pos + 128 : pos + 192;
     const int stride = pos < 32 ? 64 : pos < 48 ? 32 : 8;  // bytes
     const uint32_t e0 = (uint32_t)(sg * 8192 + (blk * 256 + base) * 2);
 #pragma unroll
     for (int k = 0; k < 5; ++k)
-      xoff[j][k] = (payload && (k < 4 || pos < 48)) ? e0 + (uint32_t)(k * stride) : (uint32_t)C::kXBytes;
+      xoff[j][k] = (valid && (k < 4 || pos < 48)) ? e0 + (uint32_t)(k * stride) : (uint32_t)C::kXBytes;
   }
 
-  // Lanes past the payload address byte 0 of the segment; their d values are
-  // 0, so whatever they sum adds exactly 0 (the sums stay finite: table
-  // values are -1, 0, 1 and activations fp16).
-  const bool active = lane < 54;
-  const int o0 = active ? 16 * lane : 0;
-  const int blk0 = o0 / kTq1Bytes;  // the lane's first block in a segment
-  int bnd = 16;                     // bytes in the first block
-#pragma unroll
-  for (int i = 0; i < 16; i += 2)
-    if ((o0 + i) / kTq1Bytes != blk0 && bnd == 16) bnd = i;
-  // per segment: the lane's first / second block slot holds a block of the segment
-  auto slot0 = [&](int sg) { return active && blk0 < (sg == KS - 1 ? nbs_last : kTq1SegBlocks); };
-  auto slot1 = [&](int sg) { return active && bnd < 16 && blk0 + 1 < (sg == KS - 1 ? nbs_last : kTq1SegBlocks); };
-  const int dof0 = blk0 * kTq1Bytes + 52;
-  const int dof1 = (bnd < 16 && blk0 + 1 < kTq1SegBlocks) ? (blk0 + 1) * kTq1Bytes + 52 : dof0;
+  // the lane's 13 bytes: segment offset s = 54 (lane / 4) + 13 (lane % 4),
+  // read from the dword at s - m (m = s % 4); its block's d at 54 (lane / 4) + 52
+  const int s0 = 54 * (lane >> 2) + 13 * (lane & 3);
+  const unsigned mis = (unsigned)(s0 & 3);
+  const int a0 = s0 - (int)mis;
+  const int dof = 54 * (lane >> 2) + 52;
 
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): table and zero element are in LDS before the barrier
   wait_vm<S::kUpFront>();              // activations (issued first) are in LDS
   __builtin_amdgcn_s_barrier();        // ... every wave's pieces too
-  // the output stage's input for the wave's rows, after the barrier's wait
-  // (the stream's later waits only get stricter by this one load)
   const auto pre = prefetch_rows(out, row0, nrows, lane);
   stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
   {
@@ -501,19 +493,17 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
     for (int j = 0; j < C::kSlots; ++j) {
       const int t = (int)threadIdx.x + j * 64 * W;
       const u32x4 v = {xe[j][0] | (xe[j][1] << 16), xe[j][2] | (xe[j][3] << 16), xe[j][4], 0u};
-      *reinterpret_cast<u32x4*>(pairs + t * 16) = v;
+      if (j + 1 < C::kSlots || t < KS * C::kEntries) *reinterpret_cast<u32x4*>(pairs + slot[j]) = v;
     }
   }
   lds_barrier();  // every pair entry is in LDS
 
-  // lanes past the payload read lane 0's pairs (finite; their d is 0)
-  const int lp = active ? lane : 0;
-  unsigned xp[KS][16][3];
+  unsigned xp[KS][13][3];
 #pragma unroll
   for (int sg = 0; sg < KS; ++sg) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(pairs + ((sg * 16 + i) * 64 + lp) * 16);
+    for (int i = 0; i < 13; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(pairs + ((sg * 13 + i) * 64 + (lane ^ (4 * i))) * 16);
       xp[sg][i][0] = v.x;
       xp[sg][i][1] = v.y;
       xp[sg][i][2] = v.z;
@@ -521,79 +511,68 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
   }
   // the lane's table copy, in the low byte of the perm source
   const unsigned colw = LREP == 16 ? (unsigned)(lane & 15) * 16u : (unsigned)(lane & 7) * 32u;
+  // byte 12 sits in the fourth dword at byte mis: perm selector putting it
+  // in byte 1 of the address, colw's byte 0 in byte 0
+  const unsigned sel12 = 0x0C0C0000u | ((4u + mis) << 8);
 
-  bool last_of_first[8];  // byte pair j is the last of the first block
-#pragma unroll
-  for (int j = 0; j < 8; ++j) last_of_first[j] = 2 * j + 2 == bnd;
-
-  // One unit's table entries and d values, read one unit ahead of its sums
-  // so that the LDS latency of unit U + 1 hides behind the arithmetic of U.
+  // One unit's table entries and d, read one unit ahead of its sums so that
+  // the LDS latency of unit U + 1 hides behind the arithmetic of unit U.
   struct UnitIn {
-    u32x4 t[16];
-    float d0, d1;
+    u32x4 t[13];
+    float d;
   };
   auto fetch = [&](auto uc) {
     constexpr int U = decltype(uc)::value, r = U / KS, sg = U % KS;
     UnitIn in;
     wait_vm<S::wait_count(U)>();
-    // refill first: the stage holds the whole run (no unread byte is
-    // overwritten) and the arithmetic stays off the load path
     stream_loads<S::issued_before(U), S::issued_before(U + 1), QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
-    // the unit's bytes in the ring: its start plus the lane's offsets, less
-    // the ring's size past its end
     constexpr int ub = S::slot_offset(r * kRowBytes + sg * kTq1SegBytes);
-    auto at = [&](int o) {
-      if constexpr (ub + kTq1SegBytes <= S::kStage) return stage + ub + o;
-      else return stage + (ub + o >= S::kStage ? ub + o - S::kStage : ub + o);
-    };
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(at(o0));
-    const unsigned short db0 = *reinterpret_cast<const unsigned short*>(at(dof0));
-    const unsigned short db1 = *reinterpret_cast<const unsigned short*>(at(dof1));
-    in.d0 = slot0(sg) ? (float)__builtin_bit_cast(_Float16, db0) : 0.f;
-    in.d1 = slot1(sg) ? (float)__builtin_bit_cast(_Float16, db1) : 0.f;
-    const unsigned dw[4] = {raw.x, raw.y, raw.z, raw.w};
+    unsigned dw[4];
+    unsigned short db;
+    if constexpr (ub + kTq1SegBytes <= S::kStage) {
+      const unsigned* p = reinterpret_cast<const unsigned*>(stage + ub + a0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      // (byte i << 8) | colw: result byte 1 = byte i & 3 of dw[i >> 2], byte 0 = colw's
-      unsigned addr = __builtin_amdgcn_perm(dw[i >> 2], colw, 0x0C0C0000u | ((4u + (i & 3)) << 8));
+      for (int j = 0; j < 4; ++j) dw[j] = p[j];
+      db = *reinterpret_cast<const unsigned short*>(stage + ub + dof);
+    } else {  // the unit wraps round the ring's end: every dword on its own
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = ub + a0 + 4 * j;
+        dw[j] = *reinterpret_cast<const unsigned*>(stage + (o >= S::kStage ? o - S::kStage : o));
+      }
+      const int o = ub + dof;
+      db = *reinterpret_cast<const unsigned short*>(stage + (o >= S::kStage ? o - S::kStage : o));
+    }
+    in.d = (float)__builtin_bit_cast(_Float16, db);
+    // bytes 4j .. 4j + 3 of the lane's run
+    const unsigned al[3] = {__builtin_amdgcn_alignbyte(dw[1], dw[0], mis),
+                            __builtin_amdgcn_alignbyte(dw[2], dw[1], mis),
+                            __builtin_amdgcn_alignbyte(dw[3], dw[2], mis)};
+#pragma unroll
+    for (int i = 0; i < 13; ++i) {
+      unsigned addr = i < 12 ? __builtin_amdgcn_perm(al[i >> 2], colw, 0x0C0C0000u | ((4u + (i & 3)) << 8))
+                             : __builtin_amdgcn_perm(dw[3], colw, sel12);
       if (LREP == 8) addr >>= 1;
       in.t[i] = *reinterpret_cast<const u32x4*>(lut + addr);
     }
     return in;
   };
-  // Sums of a unit: one short chain per byte pair (six dot2), the eight
-  // chains advanced in step so that a wave always has independent dot2s to
-  // issue, then the running total over the pairs, taken at the block
-  // boundary.
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
   auto consume = [&](auto uc, const UnitIn& in) {
     constexpr int U = decltype(uc)::value, r = U / KS, sg = U % KS;
-    float p[8];
+    float c = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = dot2h(in.t[2 * j].x, xp[sg][2 * j][0], 0.f);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = dot2h(in.t[2 * j].y, xp[sg][2 * j][1], p[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = dot2h(in.t[2 * j].z, xp[sg][2 * j][2], p[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = dot2h(in.t[2 * j + 1].x, xp[sg][2 * j + 1][0], p[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = dot2h(in.t[2 * j + 1].y, xp[sg][2 * j + 1][1], p[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = dot2h(in.t[2 * j + 1].z, xp[sg][2 * j + 1][2], p[j]);
-    float a = p[0], snap = last_of_first[0] ? p[0] : 0.f;
-#pragma unroll
-    for (int j = 1; j < 8; ++j) {
-      a += p[j];
-      snap = last_of_first[j] ? a : snap;
+    for (int i = 0; i < 13; ++i) {
+      c = dot2h(in.t[i].x, xp[sg][i][0], c);
+      c = dot2h(in.t[i].y, xp[sg][i][1], c);
+      c = dot2h(in.t[i].z, xp[sg][i][2], c);
     }
-    acc[r] = __builtin_fmaf(in.d0, snap, __builtin_fmaf(in.d1, a - snap, acc[r]));
+    acc[r] = __builtin_fmaf(in.d, c, acc[r]);
     settle(acc[r]);  // this unit's sums end before the next unit's wait
   };
   constexpr int kUnits = R * KS;
-#if QGEMV_TQ1_PIPE
   UnitIn cur = fetch(Int<0>{});
   static_for<0, kUnits>([&](auto uc) {
     constexpr int U = decltype(uc)::value;
@@ -605,9 +584,6 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_lut_kernel(const uint8_t* __r
       consume(uc, cur);
     }
   });
-#else
-  static_for<0, kUnits>([&](auto uc) { consume(uc, fetch(uc)); });
-#endif
   store_rows<R>(acc, out, pre, row0, nrows, 1.f, lane);
 }
 
@@ -738,22 +714,24 @@ static hipError_t launch_tq1_rows(const void* w, const void* x, const Out& y, in
 #endif
 
 template <int KS, int R, int W, typename Out>
-static hipError_t launch_tq1_lut_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
+static hipError_t launch_tq1_table_r(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
+                                     hipStream_t s) {
   if (k != (int64_t)KS * 4096) return hipErrorInvalidValue;  // full 16-block segments only
-  constexpr int kLrep = QGEMV_TQ1_LREP == 16 && tq1_lut_lds(KS, R, W, 16) <= 160 * 1024 ? 16 : 8;
-  static_assert(tq1_lut_lds(KS, R, W, kLrep) <= 160 * 1024, "LDS per workgroup");
+  constexpr int kLrep = QGEMV_TQ1_LREP == 16 && tq1_table_lds(KS, R, W, 16) <= 160 * 1024 ? 16 : 8;
+  static_assert(tq1_table_lds(KS, R, W, kLrep) <= 160 * 1024, "LDS per workgroup");
   const int64_t rows_per_wg = (int64_t)W * R;
   const int64_t grid = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((tq1_gemv_lut_kernel<KS, R, W, kLrep, Out>), dim3((unsigned)grid), dim3(64 * W), 0, s,
+  hipLaunchKernelGGL((tq1_gemv_table_kernel<KS, R, W, kLrep, Out>), dim3((unsigned)grid), dim3(64 * W), 0, s,
                      (const uint8_t*)w, (const uint16_t*)x, y, (int)n, (int)(k / 256));
   return hipGetLastError();
 }
 
 template <int KS, typename Out>
-static hipError_t launch_tq1_lut(const void* w, const void* x, const Out& y, int64_t n, int64_t k, hipStream_t s) {
-  constexpr int kRmax = largest_fitting_r([](int r) { return tq1_lut_lds(KS, r, 8, 8) <= 160 * 1024; });
+static hipError_t launch_tq1_table(const void* w, const void* x, const Out& y, int64_t n, int64_t k,
+                                   hipStream_t s) {
+  constexpr int kRmax = largest_fitting_r([](int r) { return tq1_table_lds(KS, r, 8, 8) <= 160 * 1024; });
   return dispatch_rows<kRmax>(n, [&](auto rc, auto wc) {
-    return launch_tq1_lut_r<KS, decltype(rc)::value, decltype(wc)::value, Out>(w, x, y, n, k, s);
+    return launch_tq1_table_r<KS, decltype(rc)::value, decltype(wc)::value, Out>(w, x, y, n, k, s);
   });
 }
 
@@ -771,7 +749,7 @@ static hipError_t launch_tq1_gemv_out(const void* w, const void* x, const Out& y
       // arithmetic kernel (one row per wave, four waves per workgroup) starts
       // faster than the table build pays off, and K = 2048 rows (half
       // segments) stay with it too
-      if (k == 4096 && n > 1024) return launch_tq1_lut<1, Out>(w, x, y, n, k, s);
+      if (k == 4096 && n > 1024) return launch_tq1_table<1, Out>(w, x, y, n, k, s);
       return launch_tq1_rows<1, Out>(w, x, y, n, k, s);
     }
     if (k <= 8192) return launch_tq1_rows<2, Out>(w, x, y, n, k, s);
