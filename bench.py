@@ -108,7 +108,7 @@ def valu_estimates(build_id: str) -> dict:
 def valu_fields(valu: dict, fmt: str, n: int, k: int, us: float) -> dict:
     """Estimated VALU issue share of one launch: the SIMD-cycles the counters
     saw spent issuing VALU instructions, per SIMD, over the launch's cycles at
-    the nominal clock (empty when no summary of this build covers the shape)."""
+    the nominal clock (empty when no counter summary of the loaded library's build id covers the shape)."""
     v = valu.get(f"{fmt}_{n}x{k}")
     if not v or "busy_cycles_per_simd" not in v:
         return {}
