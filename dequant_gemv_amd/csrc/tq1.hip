@@ -425,10 +425,10 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_table_kernel(const uint8_t* _
   const auto wr = make_rsrc(w + (int64_t)row0 * kRowBytes, (uint32_t)(nrows * kRowBytes));
   stream_loads<0, S::kUpFront, QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
 
-  // The digit table: thread t computes entry b = t % 256 and writes H = 64W /
-  // 256 ... of its copies, copy (b + H j + t / 256) % LREP on step j, so the
-  // 16 consecutive entries written by 16 consecutive lanes land in 16
-  // different bank groups.
+  // The digit table: thread t computes entry b = t % 256; the H = 64W / 256
+  // threads of an entry write LREP / H of its LREP copies each, copy
+  // (b + H j + t / 256) % LREP on step j, so the 16 consecutive entries
+  // written by 16 consecutive lanes land in 16 different bank groups.
   {
     constexpr int H = 64 * W / 256;
     const unsigned b = threadIdx.x & 255u;
