@@ -299,6 +299,33 @@ def test_nvfp4_nan_scale_poisons_only_its_row(q):
     _assert_close("nvfp4", n, k, y[keep], yr[keep], ar[keep])
 
 
+# A NaN block scale poisons its own row and no other, through every GEMV
+# kernel family: the small-shape kernels, the row-streaming kernels, and for
+# TQ1_0 the table-driven one (K = 4096, more than 1024 rows).  fp16 0x7E00
+# is a quiet NaN; the byte offsets are the block's d (Q4_K: d at 0, dmin at
+# 2; TQ1_0: d at 52).
+NAN_D_CASES = [
+    ("q4k", 9, 4096, 0), ("q4k", 2100, 4096, 0), ("q4k", 2100, 4096, 2),
+    ("tq1", 9, 4096, 52), ("tq1", 2100, 4096, 52), ("tq1", 3001, 8192, 52),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,field", NAN_D_CASES)
+def test_nan_block_scale_poisons_only_its_row(q, fmt, n, k, field):
+    w = synth.weights(fmt, n, k, 67 + n % 7)
+    x = synth.activations(fmt, k, 68)
+    bsz = 144 if fmt == "q4k" else 54
+    row, blk = n // 2 + 1, (k // 256) // 2 + 1
+    off = (row * (k // 256) + blk) * bsz + field
+    flat = w.reshape(-1)  # a view: the rows are contiguous
+    flat[off], flat[off + 1] = 0x00, 0x7E
+    y = _run_gemv(q, fmt, w, x, n, k)
+    yr, ar = oracle.gemv(fmt, w, x, n, k)
+    assert np.isnan(y[row]) and np.isnan(yr[row])
+    keep = np.arange(n) != row
+    _assert_close(fmt, n, k, y[keep], yr[keep], ar[keep])
+
+
 def test_read_ceiling_folds_every_byte(q):
     nbytes = 3 * 32768 + 4096  # ragged last workgroup
     rng = np.random.default_rng(12)
