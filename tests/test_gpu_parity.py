@@ -326,6 +326,23 @@ def test_nan_block_scale_poisons_only_its_row(q, fmt, n, k, field):
     _assert_close(fmt, n, k, y[keep], yr[keep], ar[keep])
 
 
+# TQ1_0 payload bytes drawn uniformly over all 256 values (the encoder only
+# makes 243 of them, 81 for qh), so every entry of the table-driven kernel's
+# digit table and every byte value of the arithmetic digits is exercised;
+# d stays a finite fp16.
+@pytest.mark.parametrize("n,k", [(9, 4096), (2100, 4096), (14336, 4096)])
+def test_tq1_gemv_every_byte_value(q, n, k):
+    rng = np.random.default_rng(69 + n)
+    w = rng.integers(0, 256, size=(n, (k // 256) * 54), dtype=np.uint8)
+    d = rng.uniform(1e-2, 5e-2, size=(n, k // 256)).astype(np.float16)
+    blocks = w.reshape(n, k // 256, 54)
+    blocks[:, :, 52:54] = d.view(np.uint8).reshape(n, k // 256, 2)
+    x = synth.activations("tq1", k, 70)
+    y = _run_gemv(q, "tq1", w, x, n, k)
+    yr, ar = oracle.gemv("tq1", w, x, n, k)
+    _assert_close("tq1", n, k, y, yr, ar)
+
+
 def test_read_ceiling_folds_every_byte(q):
     nbytes = 3 * 32768 + 4096  # ragged last workgroup
     rng = np.random.default_rng(12)
