@@ -3,8 +3,9 @@ library's own 32 MiB device array instead of a caller workspace.  Through the
 C ABI, two calls in a row (the second smaller, on an array the first left full
 of partial sums) must match qgemm_q4k_ws with a fresh NaN-filled workspace bit
 for bit, and sampled outputs of each must meet the oracle's prefill bar.
-Also: an unsplit call (no array used), a call on a second stream, and a call
-needing more than the array, refused with QGEMV_E_WORKSPACE.
+Also: the call captured in a HIP graph and replayed, an unsplit call (no array
+used), a call on a second stream, and a call needing more than the array,
+refused with QGEMV_E_WORKSPACE.
 """
 import numpy as np
 import pytest
@@ -51,6 +52,34 @@ def _oracle_check(wh, xh, got, t, m, k, seed):
     g = got.astype(np.float64)[np.ix_(toks, rows)]
     bad = np.argwhere(~(np.abs(g - yr) <= 1e-3 * ar + 1e-5))
     assert bad.size == 0, f"T={t} {m}x{k}: {len(bad)} sampled outputs outside the bar"
+
+
+def test_noalloc_captured_in_a_graph(q):
+    """The graph-capture use: the call recorded in a HIP graph (the first
+    no-alloc call of the process when this file runs first in it, so the
+    array's address is looked up during the capture), replayed three times
+    with eager work between the replays; every replay equals the eager call
+    bit for bit."""
+    t, m, k = 130, 4096, 4096
+    _, _, w, x = _inputs(t, m, k, 920)
+    y = _nan(t, m)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        q.qgemm_q4k_noalloc(w, x, y, t, m, k, stream=side)
+    outs = []
+    for _ in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy().copy())
+    ref = _nan(t, m)
+    q.qgemm_q4k_noalloc(w, x, ref, t, m, k)
+    torch.cuda.synchronize()
+    r = ref.cpu().numpy()
+    for i, o in enumerate(outs):
+        assert np.array_equal(o.view(np.uint32), r.view(np.uint32)), f"replay {i} differs"
 
 
 # (T, M, K): 32 MiB of partial sums (the whole array), then 24 MiB
