@@ -101,6 +101,23 @@ def test_gemv_bit_exact(q, fmt, n, k):
                            f"oracle {want[bad[0]]!r}")
 
 
+def _random_cases():
+    # shapes off the planned grid: mostly many rows, some a handful; K any
+    # multiple of the block up to 16384 (fixed seed, so the list is stable)
+    rng = np.random.default_rng(54321)
+    c = []
+    for fmt, kmul in (("q4k", 256), ("nvfp4", 32), ("tq1", 256)):
+        for _ in range(8):
+            n = int(rng.integers(1, 40000)) if rng.random() < 0.8 else int(rng.integers(1, 64))
+            c.append((fmt, n, int(rng.integers(1, 16384 // kmul + 1)) * kmul))
+    return c
+
+
+@pytest.mark.parametrize("fmt,n,k", _random_cases())
+def test_gemv_bit_exact_random_shapes(q, fmt, n, k):
+    test_gemv_bit_exact(q, fmt, n, k)
+
+
 @pytest.mark.parametrize("fmt,n,k", [("q4k", 3001, 2816), ("nvfp4", 1500, 4160), ("tq1", 13001, 2048),
                                      ("q4k", 300, 18432), ("tq1", 37, 4352)])
 @pytest.mark.parametrize("y_dtype", ["f32", "f16"])
