@@ -55,6 +55,21 @@ CASES = [
 ]
 
 
+def _random_cases():
+    # shapes off the planned grid (fixed seed, so the list is stable)
+    rng = np.random.default_rng(777)
+    c = []
+    for i in range(9):
+        fmt = ("q4k", "nvfp4", "tq1")[i % 3]
+        kmul = 64 if fmt == "nvfp4" else 256
+        t, m = int(rng.integers(1, 1500)), int(rng.integers(1, 6000))
+        c.append((fmt, t, m, int(rng.integers(1, 8192 // kmul + 1)) * kmul, 24, 48))
+    return c
+
+
+CASES += _random_cases()
+
+
 def _sample(t, m, st, sr, seed):
     rng = np.random.default_rng(seed)
     toks = np.arange(t) if st is None else np.unique(np.concatenate([[0, t - 1], rng.integers(0, t, st)]))
