@@ -377,17 +377,18 @@ struct Tq1TableRows {
   static constexpr int kXBytes = KS * 8192;
   static constexpr int kEntries = 13 * 64;  // activation pair entries (byte, lane) per segment
   static constexpr int kPairBytes = KS * kEntries * 16;
-  static constexpr int kSlots = (KS * kEntries + 64 * W - 1) / (64 * W);  // entries built per thread
-  static constexpr int kLds = kLutBytes + W * S::kStage + kXBytes + 16 + kPairBytes;  // + a zero element
+  static constexpr int kBuildersPerWave = KS * 16 * 7 / W;  // pair build tasks: 28 per block, 4 per builder
+  static constexpr int kLds = kLutBytes + W * S::kStage + kXBytes + kPairBytes;
   static_assert(LREP == 8 || LREP == 16, "table copies");
   static_assert(W == 4 || W == 8, "waves per workgroup");
+  static_assert((8 * KS) % W == 0 && kBuildersPerWave <= 64, "whole pieces of x per wave");
 };
 
 // LDS bytes of a table-driven launch (what the launcher checks against the
 // 160 KiB of a workgroup).
 constexpr int tq1_table_lds(int ks, int r, int w, int lrep) {
   const int loads = (r * ks * kTq1SegBytes + 1023) / 1024;
-  return 256 * 16 * lrep + w * (loads < kTq1Ring ? loads : kTq1Ring) * 1024 + ks * 8192 + 16 + ks * 13 * 64 * 16;
+  return 256 * 16 * lrep + w * (loads < kTq1Ring ? loads : kTq1Ring) * 1024 + ks * 8192 + ks * 13 * 64 * 16;
 }
 
 // fp16 bits of digit_k(b) - 1 for k = 0..4 (same recurrence as tq1_digits on
@@ -412,14 +413,16 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_table_kernel(const uint8_t* _
   constexpr int kRowBytes = KS * kTq1SegBytes;  // nb == 16 KS, checked by the launcher
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
   unsigned char* const lut = lds;
-  unsigned char* const xs = lds + C::kLutBytes + W * S::kStage;  // x, then a zero element
-  unsigned char* const pairs = xs + C::kXBytes + 16;
+  unsigned char* const xs = lds + C::kLutBytes + W * S::kStage;  // x
+  unsigned char* const pairs = xs + C::kXBytes;
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   unsigned char* const stage = lds + C::kLutBytes + wave * S::kStage;
   const int row0 = (blockIdx.x * W + wave) * R;
   const int nrows = max(0, min(R, n - row0));
 
+  // x into LDS in 1 KiB pieces (two blocks each): this wave copies pieces
+  // i W + wave
   load_shared_pieces<8 * KS, W>(make_rsrc(x, (uint32_t)nb * 512u), xs, wave, lane,
                                 [](int piece, int i) { return (uint32_t)(piece * 1024 + 16 * i); });
   const auto wr = make_rsrc(w + (int64_t)row0 * kRowBytes, (uint32_t)(nrows * kRowBytes));
@@ -442,34 +445,6 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_table_kernel(const uint8_t* _
       *reinterpret_cast<u32x4*>(lut + b * (16 * LREP) + copy * 16) = v;
     }
   }
-  if (threadIdx.x == 0) *reinterpret_cast<unsigned*>(xs + C::kXBytes) = 0u;
-
-  // Activation pairs of entry (byte i, lane l) of segment sg: lane l's byte
-  // i is payload byte pos = 13 (l % 4) + i of block l / 4, whose digit k
-  // feeds element base + k * stride of the block (qs[0..31]: pos, 32;
-  // qs[32..47]: pos + 128, 16; qh: pos + 192, 4 with no fifth digit, which
-  // reads the zero element).  The entry sits in slot (sg * 13 + i) * 64 +
-  // (l ^ 4 i): a lane's reads of its 13 entries stay conflict-free, and the
-  // builders (thread t makes the entry of payload byte t % 52 of block t /
-  // 52, so the 64 lanes of a build step read about 64 different x words)
-  // write 16 different 16-byte bank groups per 16 lanes.
-  uint32_t xoff[C::kSlots][5];
-  uint32_t slot[C::kSlots];
-#pragma unroll
-  for (int j = 0; j < C::kSlots; ++j) {
-    const int t = (int)threadIdx.x + j * 64 * W;
-    const int bg = t / 52, pos = t - 52 * bg;
-    const int sg = bg >> 4, blk = bg & 15;
-    const int q = pos / 13, i = pos - 13 * q;
-    slot[j] = (uint32_t)(((sg * 13 + i) * 64 + ((blk * 4 + q) ^ (4 * i))) * 16);
-    const bool valid = t < KS * C::kEntries;
-    const int base = pos < 32 ? pos : pos < 48 ? pos + 128 : pos + 192;
-    const int stride = pos < 32 ? 64 : pos < 48 ? 32 : 8;  // bytes
-    const uint32_t e0 = (uint32_t)(sg * 8192 + (blk * 256 + base) * 2);
-#pragma unroll
-    for (int k = 0; k < 5; ++k)
-      xoff[j][k] = (valid && (k < 4 || pos < 48)) ? e0 + (uint32_t)(k * stride) : (uint32_t)C::kXBytes;
-  }
 
   // the lane's 13 bytes: segment offset s = 54 (lane / 4) + 13 (lane % 4),
   // read from the dword at s - m (m = s % 4); its block's d at 54 (lane / 4) + 52
@@ -478,25 +453,65 @@ __global__ __launch_bounds__(64 * W) void tq1_gemv_table_kernel(const uint8_t* _
   const int a0 = s0 - (int)mis;
   const int dof = 54 * (lane >> 2) + 52;
 
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): table and zero element are in LDS before the barrier
-  wait_vm<S::kUpFront>();              // activations (issued first) are in LDS
-  __builtin_amdgcn_s_barrier();        // ... every wave's pieces too
-  const auto pre = prefetch_rows(out, row0, nrows, lane);
-  stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
-  {
-    unsigned xe[C::kSlots][5];
+  // Activation pairs of entry (byte i, lane l) of segment sg: lane l's byte
+  // i is payload byte pos = 13 (l % 4) + i of block l / 4, whose digit k
+  // feeds element e_k of the block: pos + 32 k for qs[0..31], pos + 128 +
+  // 16 k for qs[32..47], pos + 192 + 4 k (k < 4, no fifth digit) for qh.
+  // The entry (x[e0], x[e1]), (x[e2], x[e3]), (x[e4] or 0) sits in slot
+  // (sg * 13 + i) * 64 + (l ^ 4 i), so a lane's reads of its 13 entries are
+  // conflict-free.  A build task (block, g, j) makes the entries of payload
+  // bytes 8 g + 2 j and 8 g + 2 j + 1 (g < 6, j < 4; for g = 6, bytes 48 +
+  // 2 j and 48 + 2 j + 1, j < 2): digit k of the two bytes reads the two
+  // halves of one dword of x, elements 2 j and 2 j + 1 of the run that
+  // starts at 8 g + 32 k (g < 4), 128 + 8 g + 16 k (g = 4, 5) or 240 + 4 k
+  // (g = 6).  The 28 tasks of a block run in the wave that copied the
+  // block's piece of x, so that wave's own wait for its copy stands in for a
+  // workgroup barrier: task t of the wave (lane t % 64 in round t / 64)
+  // serves block 2 P + (t % 56) / 28 (counted over the segments) of piece
+  // P = (t / 56) W + wave, g = (t % 28) / 4, j = t % 4.
+  constexpr int kTasks = 4 * C::kBuildersPerWave, kRounds = (kTasks + 63) / 64;
+  unsigned xof[kRounds][5];   // LDS offsets in x of the task's dwords
+  unsigned slot[kRounds][2];  // and of its two entries
 #pragma unroll
-    for (int j = 0; j < C::kSlots; ++j)
+  for (int r = 0; r < kRounds; ++r) {
+    const int t = 64 * r + lane;
+    const int bblk = 2 * ((t / 56) * W + wave) + (t % 56) / 28, g = (t % 28) / 4, j = t % 4;
 #pragma unroll
-      for (int k = 0; k < 5; ++k) xe[j][k] = *reinterpret_cast<const unsigned short*>(xs + xoff[j][k]);
+    for (int k = 0; k < 5; ++k) {
+      const int e = g < 4 ? 8 * g + 32 * k : g < 6 ? 128 + 8 * g + 16 * k : k < 4 ? 240 + 4 * k : 240;
+      xof[r][k] = (unsigned)(bblk * 512 + 2 * (e + 2 * j));
+      settle(xof[r][k]);  // computed while the copies are in flight
+    }
 #pragma unroll
-    for (int j = 0; j < C::kSlots; ++j) {
-      const int t = (int)threadIdx.x + j * 64 * W;
-      const u32x4 v = {xe[j][0] | (xe[j][1] << 16), xe[j][2] | (xe[j][3] << 16), xe[j][4], 0u};
-      if (j + 1 < C::kSlots || t < KS * C::kEntries) *reinterpret_cast<u32x4*>(pairs + slot[j]) = v;
+    for (int h = 0; h < 2; ++h) {
+      const int pos = 8 * g + 2 * j + h, q = pos / 13, i13 = pos - 13 * q;
+      slot[r][h] = (unsigned)((((bblk >> 4) * 13 + i13) * 64 + (((bblk & 15) * 4 + q) ^ (4 * i13))) * 16);
+      settle(slot[r][h]);
     }
   }
-  lds_barrier();  // every pair entry is in LDS
+
+  wait_vm<S::kUpFront>();  // this wave's pieces of x (copied first) are in LDS
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int t = 64 * r + lane;
+    const int g = (t % 28) / 4, j = t % 4;
+    if (t < kTasks && (g < 6 || j < 2)) {
+      unsigned d[5];
+#pragma unroll
+      for (int k = 0; k < 5; ++k) d[k] = *reinterpret_cast<const unsigned*>(xs + xof[r][k]);
+      if (g == 6) d[4] = 0u;  // the qh bytes have no fifth digit
+      // entry 2 j from the low halves, entry 2 j + 1 from the high ones
+      const u32x4 lo = {__builtin_amdgcn_perm(d[1], d[0], 0x05040100u), __builtin_amdgcn_perm(d[3], d[2], 0x05040100u),
+                        d[4] & 0xFFFFu, 0u};
+      const u32x4 hi = {__builtin_amdgcn_perm(d[1], d[0], 0x07060302u), __builtin_amdgcn_perm(d[3], d[2], 0x07060302u),
+                        d[4] >> 16, 0u};
+      *reinterpret_cast<u32x4*>(pairs + slot[r][0]) = lo;
+      *reinterpret_cast<u32x4*>(pairs + slot[r][1]) = hi;
+    }
+  }
+  lds_barrier();  // the table and every pair entry are in LDS
+  const auto pre = prefetch_rows(out, row0, nrows, lane);
+  stream_loads<S::kUpFront, S::issued_before(0), QGEMV_WLOAD_AUX, S::kRing>(wr, stage, lane);
 
   unsigned xp[KS][13][3];
 #pragma unroll
